@@ -1,0 +1,296 @@
+"""Seeded synthetic inputs for the target-side verification step.
+
+This module is shared by the fp64 oracle's tests and by the GPU-side tests and
+benchmark.  It builds *inputs only* and holds none of the verification
+arithmetic (no accept test, no residual, no inverse-CDF sampling):
+
+* ``hidden`` and ``W`` are Gaussian draws rounded to bfloat16 (round to
+  nearest, ties to even) and stored as raw uint16 bit patterns.  Both sides of
+  the parity check read these exact bf16 values.
+* ``q`` (the drafter's distribution at each drafted position) is built from an
+  fp32 approximation of the target logits plus Gaussian noise, softmaxed.  The
+  approximation only shapes the input: neither side's logits come from here.
+* draft tokens are drawn from ``q`` with the Gumbel-max trick, a sampling
+  method deliberately different from the inverse CDF the verifier uses.
+* ``uniforms`` are ``1 - U`` with ``U`` in [0, 1) from a Philox stream, so
+  every uniform lies in (0, 1].  Slots ``0..gamma-1`` feed the accept tests,
+  slot ``gamma`` the one replacement/bonus draw.
+
+Every tensor has its own stream spawned from ``SeedSequence(seed)`` (SFC64
+for the bulk Gaussian tensors, Philox for the uniforms and the cluster
+permutation), so changing one shape never shifts another tensor's values.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+STREAMS = ("W", "hidden", "noise", "drafts", "uniforms", "clusters")
+W_CHUNK_ROWS = 16384
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Shape and value recipe of one synthetic verification workload."""
+
+    name: str
+    B: int          # sequences
+    gamma: int      # drafted tokens per sequence
+    d: int          # hidden size
+    V: int          # vocabulary size
+    w_std: float    # std of the LM-head weights
+    h_std: float    # std of the hidden states
+    sigma: float    # std of the noise added to the logits to form q
+    sparse: Optional[Tuple[int, int, int]] = None  # (clusters, cluster size, top-k clusters)
+    seed: int = 0
+
+    @property
+    def R(self) -> int:
+        return self.B * (self.gamma + 1)
+
+
+def _registry() -> Dict[str, Config]:
+    reg = {}
+    # Tiny check case: V=32, d=16, unit-variance weights and hidden states.
+    reg["tiny"] = Config("tiny", 1, 4, 16, 32, 1.0, 1.0, 1.0)
+    # Gemma-4-E2B-shaped head: d=1536, V=262144.
+    reg["gemma_e2b"] = Config("gemma_e2b", 1, 4, 1536, 262144, 0.02, 1.0, 0.5)
+    # Llama-3.1-8B-shaped head: d=4096, V=128256, gamma x B grid.
+    for g in (2, 4, 8):
+        for b in (1, 4):
+            n = f"llama8b_g{g}_b{b}"
+            reg[n] = Config(n, b, g, 4096, 128256, 0.02, 1.0, 0.5)
+    # Batch sweep on the Llama-shaped head.
+    for b in (16, 64, 256):
+        for s in (0.2, 0.5, 1.0):
+            n = f"sweep_b{b}_s{s}"
+            reg[n] = Config(n, b, 4, 4096, 128256, 0.02, 1.0, s)
+    # Sparse-q drafter: q nonzero only on the top-32 of 2048 random clusters.
+    reg["sparse_q"] = Config("sparse_q", 8, 4, 1536, 262144, 0.02, 1.0, 0.5,
+                             sparse=(2048, 128, 32))
+    return reg
+
+
+CONFIGS: Dict[str, Config] = _registry()
+
+
+def streams(seed: int) -> Dict[str, np.random.Generator]:
+    """One independent generator per tensor, spawned from ``SeedSequence(seed)``.
+
+    The bulk Gaussian tensors use SFC64 for speed; the uniforms (and the
+    cluster permutation) use Philox.
+    """
+    children = np.random.SeedSequence(seed).spawn(len(STREAMS))
+    out = {}
+    for n, c in zip(STREAMS, children):
+        bitgen = np.random.Philox if n in ("uniforms", "clusters") else np.random.SFC64
+        out[n] = np.random.Generator(bitgen(c))
+    out["_W_seedseq"] = children[STREAMS.index("W")]
+    return out
+
+
+def _round_bf16_inplace(buf: np.ndarray, scratch: np.ndarray, out: np.ndarray) -> None:
+    """Round fp32 ``buf`` to bf16 (nearest, ties to even) into uint16 ``out``.
+
+    ``buf`` is overwritten; ``scratch`` is a uint32 array of the same shape.
+    """
+    u = buf.view(np.uint32)
+    np.right_shift(u, np.uint32(16), out=scratch)
+    scratch &= np.uint32(1)
+    scratch += np.uint32(0x7FFF)
+    u += scratch
+    u >>= np.uint32(16)
+    np.copyto(out, u, casting="unsafe")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bfloat16 (nearest, ties to even); return the uint16 bits.
+
+    Inputs here are finite Gaussian draws, so NaN/Inf handling is not needed.
+    """
+    buf = np.array(x, dtype=np.float32, copy=True, order="C")
+    out = np.empty(buf.shape, dtype=np.uint16)
+    _round_bf16_inplace(buf, np.empty(buf.shape, dtype=np.uint32), out)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+_tls = threading.local()
+
+
+def _scratch(name: str, shape, dtype) -> np.ndarray:
+    """Per-thread reusable buffer (fresh pages are slow to fault in)."""
+    key = (name, np.dtype(dtype).str)
+    store = getattr(_tls, "bufs", None)
+    if store is None:
+        store = _tls.bufs = {}
+    n = int(np.prod(shape))
+    buf = store.get(key)
+    if buf is None or buf.size < n:
+        buf = store[key] = np.empty(n, dtype=dtype)
+    return buf[:n].reshape(shape)
+
+
+def _pool_map(fn, items):
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        return list(ex.map(fn, items))
+
+
+def _gumbel_draw(rng: np.random.Generator, q_row: np.ndarray) -> int:
+    """One draw from q_row by Gumbel-max: argmax_j log q_j + G_j."""
+    u = rng.random(q_row.shape[0])  # [0, 1); u == 0 gives -inf and is never chosen
+    with np.errstate(divide="ignore"):
+        keys = np.log(q_row.astype(np.float64)) - np.log(-np.log(u))
+    return int(np.argmax(keys))
+
+
+def _softmax_f64(z: np.ndarray) -> np.ndarray:
+    z = z.astype(np.float64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def make_weights(cfg: Config, rs: Dict[str, np.random.Generator]) -> np.ndarray:
+    """bf16 weights [V, d] ~ N(0, w_std^2), one SFC64 stream per 16384-row chunk."""
+    n_chunks = -(-cfg.V // W_CHUNK_ROWS)
+    seeds = rs["_W_seedseq"].spawn(n_chunks)
+    W = np.empty((cfg.V, cfg.d), dtype=np.uint16)
+
+    def work(ci):
+        v0 = ci * W_CHUNK_ROWS
+        v1 = min(cfg.V, v0 + W_CHUNK_ROWS)
+        buf = _scratch("wf", (v1 - v0, cfg.d), np.float32)
+        np.random.Generator(np.random.SFC64(seeds[ci])).standard_normal(out=buf, dtype=np.float32)
+        buf *= np.float32(cfg.w_std)
+        _round_bf16_inplace(buf, _scratch("wu", buf.shape, np.uint32), W[v0:v1])
+
+    _pool_map(work, range(n_chunks))
+    return W
+
+
+def approx_target_logits(hidden_bits: np.ndarray, W_bits: np.ndarray) -> np.ndarray:
+    """fp32 library matmul of the bf16 inputs, used only to shape q."""
+    H = bf16_bits_to_f32(hidden_bits.reshape(-1, hidden_bits.shape[-1]))
+    V, d = W_bits.shape
+    out = np.empty((H.shape[0], V), dtype=np.float32)
+    chunk = 4096
+
+    def work(v0):
+        v1 = min(V, v0 + chunk)
+        wu = _scratch("au", (v1 - v0, d), np.uint32)
+        np.copyto(wu, W_bits[v0:v1], casting="unsafe")
+        wu <<= np.uint32(16)
+        out[:, v0:v1] = H @ wu.view(np.float32).T
+
+    _pool_map(work, range(0, V, chunk))
+    return out
+
+
+def generate(cfg: Config, W_bits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Build one batch of inputs for ``cfg``.
+
+    Returns uint16 ``hidden_bits`` [B, gamma+1, d], uint16 ``W_bits`` [V, d],
+    int32 ``draft`` [B, gamma], float32 ``q`` [B, gamma, V] and float32
+    ``uniforms`` [B, gamma+1].  ``W_bits`` may be passed in to reuse a
+    previously generated weight matrix of the same config and seed.
+    """
+    rs = streams(cfg.seed)
+    B, g, d, V = cfg.B, cfg.gamma, cfg.d, cfg.V
+    if W_bits is None:
+        W_bits = make_weights(cfg, rs)
+    assert W_bits.shape == (V, d) and W_bits.dtype == np.uint16
+    hidden = f32_to_bf16_bits(
+        rs["hidden"].standard_normal((B, g + 1, d), dtype=np.float32) * np.float32(cfg.h_std))
+
+    # q is only needed at the gamma drafted positions of every sequence.
+    lg = approx_target_logits(hidden[:, :g, :], W_bits).reshape(B, g, V)
+    q = np.empty((B, g, V), dtype=np.float32)
+    if cfg.sparse is None:
+        for b in range(B):
+            noise = rs["noise"].standard_normal((g, V), dtype=np.float32) * np.float32(cfg.sigma)
+            q[b] = _softmax_f64(lg[b] + noise).astype(np.float32)
+    else:
+        n_clusters, size, top = cfg.sparse
+        assert n_clusters * size == V
+        members = rs["clusters"].permutation(V).reshape(n_clusters, size)
+        centroids = np.empty((n_clusters, d), dtype=np.float32)
+        for c in range(n_clusters):
+            centroids[c] = bf16_bits_to_f32(W_bits[members[c]]).mean(axis=0)
+        hf = bf16_bits_to_f32(hidden.reshape(-1, d)).reshape(B, g + 1, d)
+        for b in range(B):
+            noise = rs["noise"].standard_normal((g, V), dtype=np.float32) * np.float32(cfg.sigma)
+            for i in range(g):
+                score = centroids @ hf[b, i]
+                chosen = np.argsort(-score, kind="stable")[:top]
+                sel = np.sort(members[chosen].ravel())
+                row = np.zeros(V, dtype=np.float32)
+                row[sel] = _softmax_f64(lg[b, i, sel] + noise[i, sel]).astype(np.float32)
+                q[b, i] = row
+
+    draft = np.empty((B, g), dtype=np.int32)
+    for b in range(B):
+        for i in range(g):
+            draft[b, i] = _gumbel_draw(rs["drafts"], q[b, i])
+    uniforms = (np.float32(1.0) - rs["uniforms"].random((B, g + 1), dtype=np.float32)).astype(np.float32)
+    return {"hidden_bits": hidden, "W_bits": W_bits, "draft": draft, "q": q, "uniforms": uniforms}
+
+
+def custom(B: int, gamma: int, d: int, V: int, *, w_std: float = 0.5, h_std: float = 1.0,
+           sigma: float = 0.7, seed: int = 0, sparse=None) -> Dict[str, np.ndarray]:
+    """Inputs of an arbitrary (small) shape with the same recipe."""
+    return generate(Config(f"custom_B{B}_g{gamma}_d{d}_V{V}", B, gamma, d, V, w_std, h_std,
+                           sigma, sparse=sparse, seed=seed))
+
+
+def repeated_trials(base: Dict[str, np.ndarray], n: int, seed: int, *,
+                    row: int = 0) -> Dict[str, np.ndarray]:
+    """``n`` independent trials of one sequence of ``base``.
+
+    Every trial shares the hidden states, weights and q of sequence ``row``;
+    the draft tokens (drawn from q) and the uniforms are fresh per trial.
+    """
+    rs = streams(seed)
+    g = base["draft"].shape[1]
+    hidden = np.repeat(base["hidden_bits"][row:row + 1], n, axis=0)
+    q = np.repeat(base["q"][row:row + 1], n, axis=0)
+    # Gumbel-max for all trials at once (small V only).
+    V = q.shape[-1]
+    u = rs["drafts"].random((n, g, V))
+    with np.errstate(divide="ignore"):
+        keys = np.log(q.astype(np.float64)) - np.log(-np.log(u))
+    draft = np.argmax(keys, axis=-1).astype(np.int32)
+    uniforms = (np.float32(1.0) - rs["uniforms"].random((n, g + 1), dtype=np.float32)).astype(np.float32)
+    return {"hidden_bits": hidden, "W_bits": base["W_bits"], "draft": draft, "q": q,
+            "uniforms": uniforms}
+
+
+def iid_positions(V: int, d: int, gamma: int, n: int, seed: int, *, sigma: float = 1.0,
+                  w_std: float = 1.0) -> Dict[str, np.ndarray]:
+    """Trials in which every position is equally easy to guess.
+
+    All gamma+1 hidden rows are the same vector and all gamma q rows are the
+    same distribution, so every position has the same acceptance rate.
+    """
+    rs = streams(seed)
+    W = f32_to_bf16_bits(rs["W"].standard_normal((V, d), dtype=np.float32) * np.float32(w_std))
+    h = f32_to_bf16_bits(rs["hidden"].standard_normal((d,), dtype=np.float32))
+    lg = approx_target_logits(h[None, :], W)[0]
+    q1 = _softmax_f64(lg + rs["noise"].standard_normal(V, dtype=np.float32) * np.float32(sigma))
+    q1 = q1.astype(np.float32)
+    hidden = np.broadcast_to(h, (n, gamma + 1, d)).copy()
+    q = np.broadcast_to(q1, (n, gamma, V)).copy()
+    u = rs["drafts"].random((n, gamma, V))
+    with np.errstate(divide="ignore"):
+        keys = np.log(q.astype(np.float64)) - np.log(-np.log(u))
+    draft = np.argmax(keys, axis=-1).astype(np.int32)
+    uniforms = (np.float32(1.0) - rs["uniforms"].random((n, gamma + 1), dtype=np.float32)).astype(np.float32)
+    return {"hidden_bits": hidden, "W_bits": W, "draft": draft, "q": q, "uniforms": uniforms}

@@ -1,0 +1,78 @@
+"""The seeded input generator: determinism, bf16 rounding and the config recipes."""
+
+import numpy as np
+import pytest
+import torch
+
+from synth import inputs as I
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(200_000).astype(np.float32) * s for s in (1e-3, 1, 1e3)])
+    # exact ties: low 16 bits 0x8000, both parities of bit 16
+    ties = (np.arange(1000, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32) + 0x3F800000
+    x = np.concatenate([x, ties.view(np.float32)])
+    ours = I.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_deterministic_and_shapes():
+    a = I.custom(3, 4, 40, 500, seed=7)
+    b = I.custom(3, 4, 40, 500, seed=7)
+    c = I.custom(3, 4, 40, 500, seed=8)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+    assert not np.array_equal(a["W_bits"], c["W_bits"])
+    assert a["hidden_bits"].shape == (3, 5, 40) and a["hidden_bits"].dtype == np.uint16
+    assert a["W_bits"].shape == (500, 40) and a["W_bits"].dtype == np.uint16
+    assert a["draft"].shape == (3, 4) and a["draft"].dtype == np.int32
+    assert a["q"].shape == (3, 4, 500) and a["q"].dtype == np.float32
+    assert a["uniforms"].shape == (3, 5) and a["uniforms"].dtype == np.float32
+    assert np.all(a["uniforms"] > 0) and np.all(a["uniforms"] <= 1)
+    assert np.all((a["draft"] >= 0) & (a["draft"] < 500))
+    np.testing.assert_allclose(a["q"].sum(-1), 1.0, atol=1e-5)
+
+
+def test_tensor_streams_independent_of_other_shapes():
+    a = I.custom(2, 4, 40, 500, seed=7)
+    b = I.custom(2, 4, 40, 600, seed=7)
+    # W rows of the shared chunk and the hidden states do not depend on V
+    np.testing.assert_array_equal(a["W_bits"], b["W_bits"][:500])
+    np.testing.assert_array_equal(a["hidden_bits"], b["hidden_bits"])
+    np.testing.assert_array_equal(a["uniforms"], b["uniforms"])
+
+
+def test_weight_std_recipe():
+    x = I.custom(1, 1, 256, 4096, w_std=0.02, seed=1)
+    w = I.bf16_bits_to_f32(x["W_bits"])
+    assert abs(w.std() - 0.02) < 0.0005 and abs(w.mean()) < 0.0005
+
+
+def test_gumbel_drafts_follow_q():
+    rng = np.random.default_rng(0)
+    q = rng.dirichlet(np.ones(8)).astype(np.float32)
+    base = {"hidden_bits": np.zeros((1, 2, 8), np.uint16), "W_bits": np.zeros((8, 8), np.uint16),
+            "draft": np.zeros((1, 1), np.int32), "q": q[None, None, :], "uniforms": np.ones((1, 2), np.float32)}
+    t = I.repeated_trials(base, 200_000, seed=3)
+    freq = np.bincount(t["draft"][:, 0], minlength=8) / 200_000
+    np.testing.assert_allclose(freq, q, atol=0.004)
+
+
+def test_sparse_q_structure():
+    cfg = I.Config("sparse_small", 2, 3, 32, 64 * 16, 0.5, 1.0, 0.5, sparse=(64, 16, 4), seed=2)
+    x = I.generate(cfg)
+    nz = (x["q"] > 0).sum(-1)
+    assert np.all(nz == 4 * 16)
+    for b in range(2):
+        for i in range(3):
+            assert x["q"][b, i, x["draft"][b, i]] > 0
+
+
+def test_config_registry_shapes():
+    c = I.CONFIGS
+    assert (c["tiny"].V, c["tiny"].d, c["tiny"].gamma, c["tiny"].B) == (32, 16, 4, 1)
+    assert (c["gemma_e2b"].V, c["gemma_e2b"].d, c["gemma_e2b"].R) == (262144, 1536, 5)
+    assert c["llama8b_g8_b4"].R == 36 and c["sweep_b256_s1.0"].R == 1280
+    assert c["sparse_q"].sparse == (2048, 128, 32) and c["sparse_q"].R == 40

@@ -1,0 +1,81 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in the oracle (on the CPU, by replacing one of its
+step functions for the duration of the test) and checks that at least one pin
+from test_oracle_pins fails.  Nothing here touches the GPU path.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import verify_ref as R
+from tests import test_oracle_pins as P
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+MUTANTS = {
+    # keep iff r <= q/p instead of r <= p/q
+    "accept_inverted_ratio": ("accept_draft", lambda p, q, r: bool(r * p <= q)),
+    # strict inequality: ties reject
+    "accept_strict": ("accept_draft", lambda p, q, r: bool(r * q < p)),
+    # residual with the wrong sign
+    "residual_sign": ("draw_weights",
+                      lambda p, q: p.copy() if q is None else np.maximum(0.0, q.astype(float) - p)),
+    # replacement drawn from p instead of the residual
+    "residual_dropped": ("draw_weights", lambda p, q: p.copy()),
+    # bonus drawn from the residual of the last draft row is not expressible
+    # here; a count of all accepts instead of the leading ones is:
+    "count_not_prefix": ("first_rejection", lambda flags: int(sum(bool(f) for f in flags))),
+    # inverse CDF that takes the first C_j > t (other boundary convention)
+    "cdf_right": ("inverse_cdf",
+                  lambda w, u: (lambda C: (int(np.searchsorted(C, float(u) * C[-1], "right")),
+                                           C, float(C[-1]), float(u) * C[-1]))(np.cumsum(w))),
+    # inverse CDF without the normalisation by S
+    "cdf_unnormalised": ("inverse_cdf",
+                         lambda w, u: (lambda C: (min(int(np.searchsorted(C, float(u), "left")),
+                                                      len(w) - 1), C, float(C[-1]), float(u)))(np.cumsum(w))),
+    # softmax that forgets to subtract the log-normaliser
+    "softmax_unnormalised": ("softmax_rows",
+                             lambda L: (np.exp(L - L.max(-1, keepdims=True)), L.max(-1), L.max(-1))),
+    # transposed GEMM operand order (hidden against W's columns)
+    "gemm_wrong_rows": ("lmhead_logits",
+                        lambda h, W, chunk_rows=8192: R.bf16_to_f64(h) @ R.bf16_to_f64(W)[::-1].T),
+}
+
+PINS = [
+    (P.test_page_example_keep_probabilities, ()),
+    (P.test_accept_tie_and_zero_q, ()),
+    (P.test_first_rejection_all_patterns, (4,)),
+    (P.test_page_example_completed_residual, ()),
+    (P.test_inverse_cdf_brute_force, ()),
+    (P.test_inverse_cdf_boundaries_and_u_one, ()),
+    (P.test_enumeration_page_example_emits_p, ()),
+    (P.test_one_hot_target_is_greedy_match, ()),
+    (P.test_disjoint_supports_reject_first_and_draw_from_p, ()),
+    (P.test_residual_fallback_when_q_dominates, ()),
+    (P.test_softmax_sums_to_one_and_shift_invariant, ()),
+    (P.test_softmax_two_tokens_is_logistic, ()),
+    (P.test_gemm_against_exact_triple_loop, ()),
+    (P.test_output_shape_invariants_random, ()),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(R, attr, fn)
+    caught = []
+    for pin, args in PINS:
+        try:
+            if _fails(pin, *args):
+                caught.append(pin.__name__)
+        except Exception:            # a crash under the mutant also counts as caught
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
