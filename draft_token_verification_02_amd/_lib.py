@@ -1,0 +1,190 @@
+"""ctypes binding of libspecverify (include/specverify.h).
+
+Argument marshalling only: every step of the verification runs in the HIP
+library.  Tensors are torch tensors on one ROCm device; PyTorch provides the
+device memory and the stream.  If the library is not built this module raises
+instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_OK, SV_ERR_NULL, SV_ERR_DIMS, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_DEVICE = range(6)
+SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE = 1, 2, 4
+EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
+           "sv_accept_and_draw", "sv_debug_views")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("gamma", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("V", ctypes.c_int32)]
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_load().sv_status_string(status).decode()}")
+
+
+_LIB = None
+
+
+def _load():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        lib.sv_abi_version.restype = ctypes.c_int32
+        lib.sv_abi_version.argtypes = []
+        lib.sv_status_string.restype = ctypes.c_char_p
+        lib.sv_status_string.argtypes = [st]
+        lib.sv_workspace_bytes.restype = sz
+        lib.sv_workspace_bytes.argtypes = [Dims]
+        lib.spec_verify.restype = st
+        lib.spec_verify.argtypes = [vp, vp, vp, vp, vp, Dims, vp, vp, vp, sz, vp]
+        lib.sv_lmhead.restype = st
+        lib.sv_lmhead.argtypes = [vp, vp, Dims, vp, sz, vp]
+        lib.sv_accept_and_draw.restype = st
+        lib.sv_accept_and_draw.argtypes = [vp, vp, vp, Dims, vp, vp, vp, sz, vp]
+        lib.sv_debug_views.restype = st
+        lib.sv_debug_views.argtypes = [vp, Dims, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                       ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        if lib.sv_abi_version() != 1:
+            raise ImportError(f"{LIB_PATH}: unexpected ABI version {lib.sv_abi_version()}")
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _load()
+
+
+def dims_of(hidden, W, draft=None) -> Dims:
+    B, g1, d = hidden.shape
+    return Dims(B, g1 - 1, d, W.shape[0])
+
+
+def workspace_bytes(dims: Dims) -> int:
+    return int(_load().sv_workspace_bytes(dims))
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device, stream) -> ctypes.c_void_p:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_inputs(hidden, W, draft=None, q=None, uniforms=None):
+    import torch
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a ROCm device")
+    for name, t, dt in (("hidden", hidden, (torch.bfloat16, torch.int16, torch.uint16)),
+                        ("W", W, (torch.bfloat16, torch.int16, torch.uint16)),
+                        ("draft", draft, (torch.int32,)), ("q", q, (torch.float32,)),
+                        ("uniforms", uniforms, (torch.float32,))):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, W on {dev}")
+        if t.dtype not in dt:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dt}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, g1, d = hidden.shape
+    if W.dim() != 2 or W.shape[1] != d:
+        raise ValueError(f"W must be [V, {d}], got {tuple(W.shape)}")
+    V = W.shape[0]
+    if draft is not None and tuple(draft.shape) != (B, g1 - 1):
+        raise ValueError(f"draft must be [{B}, {g1 - 1}]")
+    if q is not None and tuple(q.shape) != (B, g1 - 1, V):
+        raise ValueError(f"q must be [{B}, {g1 - 1}, {V}]")
+    if uniforms is not None and tuple(uniforms.shape) != (B, g1):
+        raise ValueError(f"uniforms must be [{B}, {g1}]")
+
+
+def new_workspace(dims: Dims, device):
+    import torch
+    n = workspace_bytes(dims)
+    if n == 0:
+        raise SVError(SV_ERR_DIMS, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def verify(hidden, W, draft, q, uniforms, *, out_tokens=None, n_accepted=None, workspace=None,
+           stream=None):
+    """The whole verification step; returns (out_tokens [B, gamma+1], n_accepted [B]).
+
+    hidden bf16 [B, gamma+1, d]; W bf16 [V, d]; draft int32 [B, gamma];
+    q float32 [B, gamma, V]; uniforms float32 [B, gamma+1] in (0, 1].
+    """
+    import torch
+    _check_inputs(hidden, W, draft, q, uniforms)
+    dims = dims_of(hidden, W)
+    dev = W.device
+    if out_tokens is None:
+        out_tokens = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((dims.B,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(dims, dev)
+    st = _load().spec_verify(_ptr(hidden), _ptr(W), _ptr(draft), _ptr(q), _ptr(uniforms), dims,
+                             _ptr(out_tokens), _ptr(n_accepted), _ptr(workspace),
+                             workspace.numel(), _stream_handle(dev, stream))
+    if st != SV_OK:
+        raise SVError(st, "spec_verify")
+    return out_tokens, n_accepted
+
+
+def lmhead(hidden, W, workspace, *, stream=None):
+    """Stage 1: logits and softmax partials into ``workspace``."""
+    _check_inputs(hidden, W)
+    dims = dims_of(hidden, W)
+    st = _load().sv_lmhead(_ptr(hidden), _ptr(W), dims, _ptr(workspace), workspace.numel(),
+                           _stream_handle(W.device, stream))
+    if st != SV_OK:
+        raise SVError(st, "sv_lmhead")
+
+
+def accept_and_draw(dims: Dims, draft, q, uniforms, out_tokens, n_accepted, workspace, *,
+                    stream=None):
+    """Stage 2: accept tests, first rejection and the draw, from stage 1's workspace."""
+    st = _load().sv_accept_and_draw(_ptr(draft), _ptr(q), _ptr(uniforms), dims, _ptr(out_tokens),
+                                    _ptr(n_accepted), _ptr(workspace), workspace.numel(),
+                                    _stream_handle(q.device, stream))
+    if st != SV_OK:
+        raise SVError(st, "sv_accept_and_draw")
+
+
+def debug_views(workspace, dims: Dims) -> dict:
+    """Views of the last call's logits [R, V], row_max [R], row_sumexp [R], status [B]."""
+    import torch
+    ptrs = [ctypes.c_void_p() for _ in range(4)]
+    st = _load().sv_debug_views(_ptr(workspace), dims, *[ctypes.byref(p) for p in ptrs])
+    if st != SV_OK:
+        raise SVError(st, "sv_debug_views")
+    R = dims.B * (dims.gamma + 1)
+    base = workspace.data_ptr()
+
+    def view(p, n, dtype, shape):
+        off = p.value - base
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return workspace[off:off + nbytes].view(dtype).view(*shape)
+
+    return {"logits": view(ptrs[0], R * dims.V, torch.float32, (R, dims.V)),
+            "row_max": view(ptrs[1], R, torch.float32, (R,)),
+            "row_sumexp": view(ptrs[2], R, torch.float32, (R,)),
+            "status": view(ptrs[3], dims.B, torch.int32, (dims.B,))}

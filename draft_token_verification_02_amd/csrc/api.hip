@@ -1,0 +1,151 @@
+// C ABI of the verification step (declared in include/specverify.h):
+// argument validation, workspace carving and kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no state.
+
+#include "sv_common.h"
+
+namespace sv {
+hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
+                         float* logits, float* part_max, float* part_sum, int NP, hipStream_t stream);
+hipError_t launch_accept(const float* logits, const float* part_max, const float* part_sum, int NP,
+                         int B, int gamma, int V, const int32_t* draft, const float* q,
+                         const float* uniforms, float* row_max, float* row_sum, int32_t* out_tokens,
+                         int32_t* n_accepted, int32_t* status, hipStream_t stream);
+hipError_t launch_draw(const float* logits, const float* q, const float* row_max, const float* row_sum,
+                       const int32_t* n_accepted, const float* uniforms, int B, int gamma, int V,
+                       int NC, double* csum, double* psum, int32_t* out_tokens, int32_t* status,
+                       hipStream_t stream);
+}  // namespace sv
+
+namespace {
+
+bool dims_ok(sv_dims d) {
+    if (!(d.B >= 1 && d.B <= (1 << 20) && d.gamma >= 1 && d.gamma <= SV_MAX_GAMMA && d.d >= 8 &&
+          d.d <= 65536 && d.d % 8 == 0 && d.V >= 1 && d.V <= (1 << 28)))
+        return false;
+    // the draw's chunk-sum grid has one workgroup per (sequence, chunk)
+    const int64_t chunks = (d.V + sv::kDrawChunk - 1) / sv::kDrawChunk;
+    return (int64_t)d.B * chunks <= INT32_MAX;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+sv_status check_workspace(const void* ws, size_t bytes, sv_dims dims) {
+    if (!ws) return SV_ERR_NULL;
+    if (!aligned(ws, 256)) return SV_ERR_ALIGN;
+    if (bytes < sv_workspace_bytes(dims)) return SV_ERR_WORKSPACE;
+    return SV_OK;
+}
+
+sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* ws, hipStream_t s) {
+    const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
+    hipError_t e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
+                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NP, s);
+    return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
+sv_status stage2(const int32_t* draft, const float* q, const float* uniforms, sv_dims dims,
+                 int32_t* out_tokens, int32_t* n_accepted, void* ws, hipStream_t s) {
+    const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
+    hipError_t e = sv::launch_accept(at<float>(ws, L.logits), at<float>(ws, L.part_max),
+                                     at<float>(ws, L.part_sum), L.NP, dims.B, dims.gamma, dims.V,
+                                     draft, q, uniforms, at<float>(ws, L.row_max),
+                                     at<float>(ws, L.row_sum), out_tokens, n_accepted,
+                                     at<int32_t>(ws, L.status), s);
+    if (e != hipSuccess) return SV_ERR_DEVICE;
+    e = sv::launch_draw(at<float>(ws, L.logits), q, at<float>(ws, L.row_max), at<float>(ws, L.row_sum),
+                        n_accepted, uniforms, dims.B, dims.gamma, dims.V, L.NC,
+                        at<double>(ws, L.csum), at<double>(ws, L.psum), out_tokens,
+                        at<int32_t>(ws, L.status), s);
+    return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
+sv_status check_stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, const void* ws,
+                       size_t bytes) {
+    if (!dims_ok(dims)) return SV_ERR_DIMS;
+    if (!hidden || !W) return SV_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(W, 16)) return SV_ERR_ALIGN;
+    return check_workspace(ws, bytes, dims);
+}
+
+sv_status check_stage2(const int32_t* draft, const float* q, const float* uniforms, sv_dims dims,
+                       const int32_t* out_tokens, const int32_t* n_accepted, const void* ws,
+                       size_t bytes) {
+    if (!dims_ok(dims)) return SV_ERR_DIMS;
+    if (!draft || !q || !uniforms || !out_tokens || !n_accepted) return SV_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(draft, 4) || !aligned(uniforms, 4) || !aligned(out_tokens, 4) ||
+        !aligned(n_accepted, 4))
+        return SV_ERR_ALIGN;
+    return check_workspace(ws, bytes, dims);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_string(sv_status status) {
+    switch (status) {
+        case SV_OK: return "SV_OK";
+        case SV_ERR_NULL: return "SV_ERR_NULL: a required pointer is NULL";
+        case SV_ERR_DIMS: return "SV_ERR_DIMS: a dimension is outside the supported limits";
+        case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace smaller than sv_workspace_bytes(dims)";
+        case SV_ERR_ALIGN: return "SV_ERR_ALIGN: a pointer is not aligned as required";
+        case SV_ERR_DEVICE: return "SV_ERR_DEVICE: a HIP kernel launch failed";
+    }
+    return "unknown sv_status";
+}
+
+size_t sv_workspace_bytes(sv_dims dims) {
+    if (!dims_ok(dims)) return 0;
+    return sv::make_layout(dims.B, dims.gamma, dims.d, dims.V).total;
+}
+
+sv_status sv_lmhead(const uint16_t* hidden, const uint16_t* W_lmhead, sv_dims dims, void* workspace,
+                    size_t workspace_bytes, void* hip_stream) {
+    const sv_status st = check_stage1(hidden, W_lmhead, dims, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    return stage1(hidden, W_lmhead, dims, workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+sv_status sv_accept_and_draw(const int32_t* draft_tokens, const float* q, const float* uniforms,
+                             sv_dims dims, int32_t* out_tokens, int32_t* n_accepted, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+    const sv_status st = check_stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted,
+                                      workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    return stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace,
+                  static_cast<hipStream_t>(hip_stream));
+}
+
+sv_status spec_verify(const uint16_t* hidden, const uint16_t* W_lmhead, const int32_t* draft_tokens,
+                      const float* q, const float* uniforms, sv_dims dims, int32_t* out_tokens,
+                      int32_t* n_accepted, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    sv_status st = check_stage1(hidden, W_lmhead, dims, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    st = check_stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = stage1(hidden, W_lmhead, dims, workspace, s);
+    if (st != SV_OK) return st;
+    return stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace, s);
+}
+
+sv_status sv_debug_views(const void* workspace, sv_dims dims, const float** logits,
+                         const float** row_max, const float** row_sumexp, const int32_t** status) {
+    if (!dims_ok(dims)) return SV_ERR_DIMS;
+    if (!workspace) return SV_ERR_NULL;
+    const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
+    const char* base = static_cast<const char*>(workspace);
+    if (logits) *logits = reinterpret_cast<const float*>(base + L.logits);
+    if (row_max) *row_max = reinterpret_cast<const float*>(base + L.row_max);
+    if (row_sumexp) *row_sumexp = reinterpret_cast<const float*>(base + L.row_sum);
+    if (status) *status = reinterpret_cast<const int32_t*>(base + L.status);
+    return SV_OK;
+}
+
+}  // extern "C"

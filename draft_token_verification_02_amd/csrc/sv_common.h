@@ -1,0 +1,60 @@
+// Shared definitions of the verification-step kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <climits>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;              // threads per workgroup of every kernel
+constexpr int kLmTile = 16;              // vocab rows (and hidden rows) per MFMA fragment
+constexpr int kLmTilesPerWave = 4;       // vocab fragments per wave in the LM-head kernel
+constexpr int kLmVocabPerBlock = (kBlock / kWave) * kLmTilesPerWave * kLmTile;  // 256
+constexpr int kLmRowsPerPass = 64;       // hidden rows one LM-head launch handles
+constexpr int kDrawPerThread = 16;       // vocab entries per thread in the draw kernels
+constexpr int kDrawChunk = kBlock * kDrawPerThread;                             // 4096
+
+// Byte offsets of every array inside the caller's workspace.
+struct Layout {
+    int R, NP, NC;
+    size_t logits, part_max, part_sum, row_max, row_sum, status, csum, psum, total;
+};
+
+static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static inline Layout make_layout(int B, int gamma, int d, int V) {
+    (void)d;
+    Layout L;
+    L.R = B * (gamma + 1);
+    L.NP = (V + kLmVocabPerBlock - 1) / kLmVocabPerBlock;
+    L.NC = (V + kDrawChunk - 1) / kDrawChunk;
+    size_t off = 0;
+    L.logits = off;   off = align_up(off + (size_t)L.R * V * sizeof(float), 256);
+    L.part_max = off; off = align_up(off + (size_t)L.R * L.NP * sizeof(float), 256);
+    L.part_sum = off; off = align_up(off + (size_t)L.R * L.NP * sizeof(float), 256);
+    L.row_max = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
+    L.row_sum = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
+    L.status = off;   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
+    L.csum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
+    L.psum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
+    L.total = off;
+    return L;
+}
+
+// Merge of two (max, sum of exp(x - max)) pairs: the online-softmax step.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+    if (m2 == -INFINITY) return;
+    if (m == -INFINITY) { m = m2; s = s2; return; }
+    if (m2 > m) { s = s * expf(m - m2) + s2; m = m2; }
+    else        { s = s + s2 * expf(m2 - m); }
+}
+
+}  // namespace sv

@@ -1,0 +1,135 @@
+/*
+ * specverify.h -- C ABI of the target-side verification step of speculative
+ * decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * What the step computes (per sequence b of B; R = B*(gamma+1) rows in all):
+ *
+ *   1. logits[r][v] = sum_k hidden[r][k] * W[v][k] for the gamma drafted
+ *      positions plus one, all rows in one pass over W.  W is the tied
+ *      embedding table, [V][d] row-major.  ("多詞元預測視覺化指南", section
+ *      高效嵌入器: the LM head multiplies the hidden state by the embedding
+ *      matrix; "推测解码", section 先让小模型猜: one weight read scores all
+ *      gamma+1 positions.)
+ *   2. p = softmax(logits) per row, temperature 1.
+ *   3. For each draft i < gamma with token x = draft[b][i]: keep it iff
+ *      uniforms[b][i] * q[b][i][x] <= p[row i][x]; i.e. keep outright when
+ *      q <= p, else with probability p/q.  ("推测解码", section 通过的规则.)
+ *   4. n = number of leading kept drafts; checking stops at the first
+ *      rejection.  ("推测解码", section 留下对的，换掉错的.)
+ *   5. If n < gamma the replacement is drawn from max(0, p - q) at row n,
+ *      renormalised; if n == gamma the bonus token is drawn from p at row
+ *      gamma.  The draw is an inverse CDF over ascending token id with
+ *      u = uniforms[b][gamma]: the smallest y whose running weight sum
+ *      reaches u * (total weight).  ("推测解码", sections 通过的规则 and
+ *      留下对的，换掉错的.)
+ *   6. out_tokens[b] = draft[b][0..n-1], y, then -1 up to gamma+1 entries.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are device pointers owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t passed as void*, NULL
+ *     for the null stream) and is asynchronous: outputs are valid once the
+ *     stream reaches that point.  No host synchronisation, no copies.
+ *   - Argument errors are returned before anything is enqueued.  A failed
+ *     kernel launch returns SV_ERR_DEVICE.  Data errors are not trapped: an
+ *     out-of-range draft id is treated as rejected (p = 0) and recorded in
+ *     the per-sequence device status word (see sv_debug_views).
+ *   - Results are bitwise deterministic for identical inputs and dims.
+ *     Calls that use distinct workspaces may run concurrently.
+ *   - Shapes: B in [1, 2^20], gamma in [1, 32], d in [8, 65536] and a
+ *     multiple of 8, V in [1, 2^28], and B * ceil(V / 4096) < 2^31.  `hidden`, `W`, `q` and `workspace`
+ *     must be 16-byte aligned (workspace: 256-byte aligned).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SV_API __attribute__((visibility("default")))
+#else
+#define SV_API
+#endif
+
+#define SV_ABI_VERSION 1
+#define SV_MAX_GAMMA 32
+
+typedef struct {
+    int32_t B;      /* sequences */
+    int32_t gamma;  /* drafted tokens per sequence */
+    int32_t d;      /* hidden size */
+    int32_t V;      /* vocabulary size */
+} sv_dims;
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_NULL = 1,       /* a required pointer is NULL */
+    SV_ERR_DIMS = 2,       /* a dimension is outside the limits above */
+    SV_ERR_WORKSPACE = 3,  /* workspace smaller than sv_workspace_bytes(dims) */
+    SV_ERR_ALIGN = 4,      /* a pointer is not aligned as required */
+    SV_ERR_DEVICE = 5      /* a HIP launch failed */
+} sv_status;
+
+/* Per-sequence device status bits (int32, one word per sequence). */
+#define SV_DEV_BAD_DRAFT 1  /* a draft id outside [0, V) was seen (treated as rejected) */
+#define SV_DEV_FALLBACK 2   /* the residual summed to <= 0; the replacement was drawn from p */
+#define SV_DEV_NONFINITE 4  /* no finite positive weights at all; token 0 was emitted */
+
+/* ABI version of the loaded library (SV_ABI_VERSION). */
+SV_API int32_t sv_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+SV_API const char *sv_status_string(sv_status status);
+
+/* Bytes of device workspace one call needs for `dims`; 0 if dims are invalid.
+ * The workspace holds the fp32 logits [R][V], the per-row softmax
+ * normalisers and the draw's partial sums.  Its contents need no
+ * initialisation and are overwritten by every call. */
+SV_API size_t sv_workspace_bytes(sv_dims dims);
+
+/* The whole verification step: stage 1 then stage 2 below.
+ *   hidden       bf16 bits [B][gamma+1][d]   target final hidden states
+ *   W_lmhead     bf16 bits [V][d]            LM-head (tied embedding) weights
+ *   draft_tokens int32 [B][gamma]            drafted token ids
+ *   q            fp32 [B][gamma][V]          drafter probabilities, used as given
+ *   uniforms     fp32 [B][gamma+1] in (0,1]  [:, :gamma] accept tests, [:, gamma] the draw
+ *   out_tokens   int32 [B][gamma+1]          emitted tokens, -1 after the last
+ *   n_accepted   int32 [B]                   leading kept drafts, 0..gamma       */
+SV_API sv_status spec_verify(const uint16_t *hidden, const uint16_t *W_lmhead,
+                      const int32_t *draft_tokens, const float *q, const float *uniforms,
+                      sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
+                      void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Stage 1 alone: the LM-head GEMM for all R rows in one pass over W, writing
+ * the fp32 logits and per-tile softmax partials into the workspace.
+ * (Steps 1-2 above.) */
+SV_API sv_status sv_lmhead(const uint16_t *hidden, const uint16_t *W_lmhead, sv_dims dims,
+                    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Stage 2 alone: softmax normalisers, accept tests, first rejection and the
+ * replacement/bonus draw, from the logits stage 1 left in the same
+ * workspace with the same dims.  (Steps 2-6 above.) */
+SV_API sv_status sv_accept_and_draw(const int32_t *draft_tokens, const float *q, const float *uniforms,
+                             sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Device pointers into `workspace` for inspection after a call completes:
+ *   logits      fp32 [R][V]
+ *   row_max     fp32 [R]      max_v logits[r][v]
+ *   row_sumexp  fp32 [R]      sum_v exp(logits[r][v] - row_max[r])
+ *   status      int32 [B]     SV_DEV_* bits of the last call
+ * Any output pointer may be NULL.  Pure pointer arithmetic: enqueues nothing. */
+SV_API sv_status sv_debug_views(const void *workspace, sv_dims dims, const float **logits,
+                         const float **row_max, const float **row_sumexp,
+                         const int32_t **status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

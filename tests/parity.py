@@ -1,0 +1,136 @@
+"""Comparison of the HIP path's outputs with the fp64 oracle's.
+
+The bar (taken from the verification step's specification):
+  * logits: per row, max |dl| <= 2e-2 * max |l|  (bf16 GEMM, fp32 accumulate);
+  * p = softmax(logits): max |dp| <= 1e-5 absolute;
+  * n_accepted: identical, unless the oracle flags the first differing accept
+    test as lying within 1e-5 of its boundary (|r - p/q| < 1e-5);
+  * emitted tokens: the kept drafts and -1 padding exactly; the drawn token
+    identical unless the oracle flags the draw as lying within 1e-5 (in
+    normalised CDF units) of an interval edge -- then it must be admissible
+    (u within 1e-5 of that token's interval on the oracle's CDF).  When a
+    flagged accept test changed n, the draw is checked at the GPU's row with
+    the oracle's conditional mode.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import verify_ref as R
+
+LOGIT_RTOL = 2e-2
+P_ATOL = 1e-5
+
+
+def to_device(x: dict, dev):
+    import torch
+    t = {}
+    for k, v in x.items():
+        a = np.ascontiguousarray(v)
+        if a.dtype == np.uint16:
+            t[k] = torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            t[k] = torch.from_numpy(a).to(dev)
+    return t
+
+
+def run_gpu(x: dict, dev, *, split=False):
+    """Run the step through the C ABI; return numpy outputs and debug views."""
+    import torch
+    import draft_token_verification_02_amd as sv
+    t = to_device(x, dev)
+    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    ws = sv.new_workspace(dims, dev)
+    if split:
+        out = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+        n = torch.empty((dims.B,), dtype=torch.int32, device=dev)
+        sv.lmhead(t["hidden_bits"], t["W_bits"], ws)
+        sv.accept_and_draw(dims, t["draft"], t["q"], t["uniforms"], out, n, ws)
+    else:
+        out, n = sv.verify(t["hidden_bits"], t["W_bits"], t["draft"], t["q"], t["uniforms"],
+                           workspace=ws)
+    torch.cuda.synchronize()
+    v = sv.debug_views(ws, dims)
+    res = {"out": out.cpu().numpy(), "n": n.cpu().numpy(),
+           "logits": v["logits"].cpu().numpy(), "row_max": v["row_max"].cpu().numpy(),
+           "row_sumexp": v["row_sumexp"].cpu().numpy(), "status": v["status"].cpu().numpy()}
+    del ws, t
+    return res
+
+
+def subset(x: dict, seqs) -> dict:
+    """Inputs restricted to the sequences ``seqs`` (W shared)."""
+    seqs = np.asarray(seqs)
+    return {"hidden_bits": x["hidden_bits"][seqs], "W_bits": x["W_bits"], "draft": x["draft"][seqs],
+            "q": x["q"][seqs], "uniforms": x["uniforms"][seqs]}
+
+
+def gpu_rows(gpu: dict, seqs, g1: int) -> np.ndarray:
+    return (np.asarray(seqs)[:, None] * g1 + np.arange(g1)[None, :]).ravel()
+
+
+def compare(x: dict, gpu: dict, seqs=None, ref=None) -> dict:
+    """Assert the bar above for sequences ``seqs`` (all by default); return a report."""
+    B, g1, d = x["hidden_bits"].shape
+    g = g1 - 1
+    V = x["W_bits"].shape[0]
+    seqs = np.arange(B) if seqs is None else np.asarray(seqs)
+    xs = subset(x, seqs)
+    if ref is None:
+        ref = R.verify(xs["hidden_bits"], xs["W_bits"], xs["draft"], xs["q"], xs["uniforms"])
+    rows = gpu_rows(gpu, seqs, g1)
+    gl = gpu["logits"][rows].astype(np.float64)
+    rl = ref.logits
+
+    # logits and p
+    row_scale = np.abs(rl).max(axis=1)
+    dl = np.abs(gl - rl).max(axis=1)
+    assert np.all(dl <= LOGIT_RTOL * row_scale), f"logit error {dl.max()} vs scale {row_scale.min()}"
+    gm = gpu["row_max"][rows].astype(np.float64)
+    gs = gpu["row_sumexp"][rows].astype(np.float64)
+    gp = np.exp(gl - gm[:, None]) / gs[:, None]
+    dp = np.abs(gp - ref.p)
+    assert dp.max() <= P_ATOL, f"max |dp| = {dp.max()}"
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(ref.p > 1e-30, dp / ref.p, 0.0)
+
+    n_gpu = gpu["n"][seqs]
+    out_gpu = gpu["out"][seqs]
+    rep = {"seqs": len(seqs), "max_abs_dlogit": float(dl.max()), "max_abs_dp": float(dp.max()),
+           "max_rel_dp": float(rel.max()), "n_mismatch_flagged": 0, "draw_flagged": 0,
+           "draw_flagged_exact": 0, "draw_exact": 0, "accept_flagged": int(ref.accept_flagged.sum()),
+           "alpha_mean": float(ref.alpha.mean()), "mean_tokens": float((n_gpu + 1).mean())}
+    force = None
+    for i, b in enumerate(seqs):
+        n = int(n_gpu[i])
+        assert 0 <= n <= g
+        if n != ref.n_accepted[i]:
+            k = min(n, int(ref.n_accepted[i]))
+            assert ref.accept_flagged[i, k], (
+                f"seq {b}: n_gpu={n} n_ref={ref.n_accepted[i]} at unflagged test {k} "
+                f"(margin {ref.accept_margin[i, k]})")
+            rep["n_mismatch_flagged"] += 1
+        # kept drafts and padding are fixed by n
+        assert list(out_gpu[i, :n]) == list(x["draft"][b, :n]), f"seq {b}: kept drafts differ"
+        assert all(v == -1 for v in out_gpu[i, n + 1:]), f"seq {b}: padding"
+    if rep["n_mismatch_flagged"]:
+        force = n_gpu.copy()
+        cond = R.verify(xs["hidden_bits"], xs["W_bits"], xs["draft"], xs["q"], xs["uniforms"],
+                        force_n=force, logits=ref.logits)
+    for i, b in enumerate(seqs):
+        n = int(n_gpu[i])
+        r = ref if n == ref.n_accepted[i] else cond
+        y = int(out_gpu[i, n])
+        if not r.draw_flagged[i]:
+            assert y == r.out_tokens[i, n], (
+                f"seq {b}: token {y} vs oracle {r.out_tokens[i, n]} (margin {r.draw_margin[i]})")
+            rep["draw_exact"] += 1
+        else:
+            rep["draw_flagged"] += 1
+            rep["draw_flagged_exact"] += int(y == r.out_tokens[i, n])
+            u = float(x["uniforms"][b, g])
+            assert R.draw_admissible(r.draw_cdf[i], r.draw_S[i], u, y), (
+                f"seq {b}: flagged draw {y} not admissible (oracle {r.out_tokens[i, n]})")
+    rep["min_draw_margin"] = float(ref.draw_margin.min())
+    return rep
