@@ -8,19 +8,25 @@
 //     later drafts; when every draft passes, emit the target's own token at
 //     the extra position, which the same weight read already scored.
 //
-// Kernels (all 256 threads, enqueued in this order on one stream):
-//   accept_kernel     one workgroup per sequence: merge the LM-head tile
-//                     partials into each row's softmax normaliser, run the
-//                     gamma accept tests (r * q <= p) and find the first
-//                     rejection with a wave ballot.
-//   draw_sums_kernel  one workgroup per (sequence, 4096-token chunk): fp64
-//                     totals of the draw weights (residual or p) and of p.
-//   draw_pick_kernel  one workgroup per sequence: scan the chunk totals, find
-//                     the chunk where the running sum reaches u * S, rescan
-//                     that chunk and pick the first token that reaches it.
-// The weights are recomputed from the logits in both draw kernels with the
-// same code, and the chunk scan is the same routine, so the chunk totals the
-// second kernel walks are bitwise those the first one wrote.
+// One kernel after the LM head, one 256-thread workgroup per (sequence b,
+// 4096-token chunk c).  Every workgroup of a sequence
+//   1. gathers l[x_i], q[x_i] and r_i of the gamma drafts and, meanwhile,
+//      merges each of the sequence's gamma+1 rows' LM-head partials (one per
+//      LM-head workgroup, 16-byte loads, 32 threads per row) into the row's
+//      softmax normaliser;
+//   2. runs the gamma accept tests r * q <= p and takes n, the number of
+//      leading accepts, from a wave ballot;
+//   3. computes fp64 totals of its chunk's draw weights -- the residual
+//      max(0, p - q) at row n, or p at row gamma for the bonus -- and of p.
+// The last workgroup of the sequence to finish (a per-sequence counter that
+// the LM-head launch zeroes) writes n, the kept drafts, the padding and the
+// status, scans the chunk totals, finds the chunk where the running sum
+// reaches u * S, rescans that chunk with the same code and picks the first
+// token that reaches it: an inverse CDF over ascending token ids.
+//
+// Steps 1-2 are repeated by every chunk workgroup of a sequence; they read
+// (gamma+1) * NP * 8 bytes of partials, far less than the chunk itself, and
+// spare a kernel boundary between the accept test and the draw.
 
 #include "sv_common.h"
 
@@ -28,13 +34,18 @@ namespace sv {
 
 namespace {
 
+constexpr int kRowThreads = 32;                  // threads merging one row's partials
+constexpr int kRowsPerPass = kBlock / kRowThreads;
+constexpr int kMergeLoads = kLmMaxPartials / 4 / kRowThreads;   // float4 loads per thread per row
+
 __device__ __forceinline__ float target_prob(float logit, float row_max, float row_sum) {
     return expf(logit - row_max) / row_sum;
 }
 
 // Inclusive prefix sum of one double per thread over the workgroup, in a
 // fixed order (Hillis-Steele within each wave, then the wave totals added in
-// wave order).  Returns this thread's inclusive value; *total gets the sum.
+// wave order).  Returns this thread's inclusive value; *total gets the sum,
+// with the same association as the last thread's value.
 __device__ double block_inclusive_scan(double v, double* total) {
     __shared__ double s_wave[kBlock / kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -53,9 +64,21 @@ __device__ double block_inclusive_scan(double v, double* total) {
         all += s_wave[w];
     }
     __syncthreads();
-    // all = ((w0 + w1) + w2) + w3, the same association as the last thread's value.
     *total = all;
     return wave == 0 ? v : before + v;
+}
+
+// Exclusive prefix: the previous thread's inclusive value (never incl - own).
+__device__ double block_exclusive_scan(double v, double* total) {
+    __shared__ double s_last[kBlock / kWave];
+    const double incl = block_inclusive_scan(v, total);
+    const int lane = threadIdx.x & (kWave - 1);
+    const double up = __shfl_up(incl, 1);
+    if (lane == kWave - 1) s_last[threadIdx.x / kWave] = incl;
+    __syncthreads();
+    const double r = lane > 0 ? up : (threadIdx.x == 0 ? 0.0 : s_last[threadIdx.x / kWave - 1]);
+    __syncthreads();
+    return r;
 }
 
 __device__ __forceinline__ int block_min_int(int v) {
@@ -74,72 +97,99 @@ __device__ __forceinline__ int block_min_int(int v) {
 __device__ __forceinline__ int block_max_int(int v) { return -block_min_int(-v); }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void accept_kernel(
-    const float* __restrict__ logits, const float* __restrict__ part_max,
-    const float* __restrict__ part_sum, int NP, int gamma, int V,
-    const int32_t* __restrict__ draft, const float* __restrict__ q,
-    const float* __restrict__ uniforms, float* __restrict__ row_max, float* __restrict__ row_sum,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_accepted,
-    int32_t* __restrict__ status) {
-    __shared__ float s_m[kBlock / kWave], s_s[kBlock / kWave];
-    __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
-    const int b = blockIdx.x;
+// Steps 1-2: softmax normalisers of the sequence's rows (into r_m, r_s) and
+// the accept tests.  Returns n; *bad is set when a draft id was out of range.
+__device__ int accept_tests(const float* __restrict__ logits, const float* __restrict__ part_max,
+                            const float* __restrict__ part_sum, int NP, int NPs, int b, int gamma,
+                            int V, const int32_t* __restrict__ draft, const float* __restrict__ q,
+                            const float* __restrict__ uniforms, float* r_m, float* r_s, bool* bad) {
+    __shared__ int s_n, s_bad;
     const int g1 = gamma + 1;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
 
-    // Softmax normaliser of each of this sequence's gamma+1 rows.
-    for (int i = 0; i < g1; ++i) {
-        const size_t r = (size_t)b * g1 + i;
+    // Draft gathers, issued before the partial loads they do not depend on.
+    float lx = 0.f, qx = 0.f, ux = 1.f;
+    bool valid = false;
+    if (wave == 0 && lane < gamma) {
+        const int x = draft[(size_t)b * gamma + lane];
+        valid = x >= 0 && x < V;
+        ux = uniforms[(size_t)b * g1 + lane];
+        if (valid) {
+            lx = logits[((size_t)b * g1 + lane) * V + x];
+            qx = q[((size_t)b * gamma + lane) * V + x];
+        }
+    }
+
+    // 32 threads per row, 8 rows per pass; each thread holds at most
+    // kMergeLoads float4 of maxima and of sums, all loaded before use.
+    const int sub = threadIdx.x % kRowThreads;
+    const int grp = threadIdx.x / kRowThreads;
+    const int n4 = (NP + 3) / 4;
+    for (int i0 = 0; i0 < g1; i0 += kRowsPerPass) {
+        const int i = i0 + grp;
         float m = -INFINITY, s = 0.f;
-        for (int j = threadIdx.x; j < NP; j += kBlock) lse_merge(m, s, part_max[r * NP + j], part_sum[r * NP + j]);
+        if (i < g1) {
+            const size_t r = (size_t)b * g1 + i;
+            const float4* pm = reinterpret_cast<const float4*>(part_max + r * NPs);
+            const float4* ps = reinterpret_cast<const float4*>(part_sum + r * NPs);
+            float4 a[kMergeLoads], c[kMergeLoads];
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
+            for (int u = 0; u < kMergeLoads; ++u) {
+                const int jj = sub + u * kRowThreads;
+                a[u] = jj < n4 ? pm[jj] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                c[u] = jj < n4 ? ps[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeLoads; ++u) {
+                const int j = 4 * (sub + u * kRowThreads);     // entries past NP are padding
+                if (j + 0 < NP) m = fmaxf(m, a[u].x);
+                if (j + 1 < NP) m = fmaxf(m, a[u].y);
+                if (j + 2 < NP) m = fmaxf(m, a[u].z);
+                if (j + 3 < NP) m = fmaxf(m, a[u].w);
+            }
+            if (m != -INFINITY) {
+#pragma unroll
+                for (int u = 0; u < kMergeLoads; ++u) {
+                    const int j = 4 * (sub + u * kRowThreads);
+                    if (j + 0 < NP && a[u].x != -INFINITY) s += c[u].x * expf(a[u].x - m);
+                    if (j + 1 < NP && a[u].y != -INFINITY) s += c[u].y * expf(a[u].y - m);
+                    if (j + 2 < NP && a[u].z != -INFINITY) s += c[u].z * expf(a[u].z - m);
+                    if (j + 3 < NP && a[u].w != -INFINITY) s += c[u].w * expf(a[u].w - m);
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < kRowThreads; off <<= 1) {
             const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
             lse_merge(m, s, m2, s2);
         }
-        if (lane == 0) { s_m[wave] = m; s_s[wave] = s; }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            float M = -INFINITY, S = 0.f;
-            for (int w = 0; w < kBlock / kWave; ++w) lse_merge(M, S, s_m[w], s_s[w]);
-            r_m[i] = M; r_s[i] = S;
-            row_max[r] = M; row_sum[r] = S;
-        }
-        __syncthreads();
+        if (sub == 0 && i < g1) { r_m[i] = m; r_s[i] = s; }
     }
+    __syncthreads();
 
     if (wave == 0) {
         bool keep = false;
-        int flags = 0;
-        if (lane < gamma) {
-            const int x = draft[(size_t)b * gamma + lane];
-            if (x >= 0 && x < V) {
-                const size_t r = (size_t)b * g1 + lane;
-                const float p = target_prob(logits[r * V + x], r_m[lane], r_s[lane]);
-                const float qx = q[((size_t)b * gamma + lane) * V + x];
-                keep = uniforms[(size_t)b * g1 + lane] * qx <= p;
-            } else {
-                flags = SV_DEV_BAD_DRAFT;
-            }
-        }
+        if (lane < gamma && valid) keep = ux * qx <= target_prob(lx, r_m[lane], r_s[lane]);
         const unsigned long long kept = __ballot(keep);
-        const int n = min(__builtin_ctzll(~kept), gamma);
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) flags |= __shfl_xor(flags, off);
-        if (lane == 0) { n_accepted[b] = n; status[b] = flags; }
-        if (lane < g1 && lane != n)
-            out_tokens[(size_t)b * g1 + lane] = lane < n ? draft[(size_t)b * gamma + lane] : -1;
+        const unsigned long long badm = __ballot(lane < gamma && !valid);
+        if (lane == 0) {
+            s_n = min(__builtin_ctzll(~kept), gamma);
+            s_bad = badm != 0;
+        }
     }
+    __syncthreads();
+    *bad = s_bad;
+    return s_n;
 }
 
 // ---------------------------------------------------------------------------
 // The row a sequence draws from: its logits, the q of the rejected draft
 // (nullptr for the bonus draw), and its softmax normaliser.
 struct DrawRow {
-    const float* lrow;   // logits of the draw row
-    const float* qrow;   // q of the rejected draft, or nullptr for the bonus
-    float M, S;          // softmax normaliser of the draw row
+    const float* lrow;
+    const float* qrow;
+    float M, S;
     int V;
 };
 
@@ -152,7 +202,10 @@ __device__ __forceinline__ void load16(const float* row, int j0, int V, float (&
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < kDrawPerThread; ++e) x[e] = j0 + e < V ? row[j0 + e] : 0.f;
+        for (int e = 0; e < kDrawPerThread; ++e) x[e] = 0.f;
+#pragma unroll
+        for (int e = 0; e < kDrawPerThread; ++e)
+            if (j0 + e < V) x[e] = row[j0 + e];
     }
 }
 
@@ -171,65 +224,11 @@ __device__ __forceinline__ void draw_weights16(const DrawRow& d, int j0, float (
     }
 }
 
-__device__ __forceinline__ DrawRow draw_row(const float* logits, const float* q, const float* row_max,
-                                            const float* row_sum, const int32_t* n_accepted,
-                                            int b, int gamma, int V) {
-    const int n = n_accepted[b];
-    const size_t k = (size_t)b * (gamma + 1) + n;
-    DrawRow d;
-    d.lrow = logits + k * V;
-    d.qrow = n < gamma ? q + ((size_t)b * gamma + n) * V : nullptr;
-    d.M = row_max[k];
-    d.S = row_sum[k];
-    d.V = V;
-    return d;
-}
-
-__global__ __launch_bounds__(kBlock) void draw_sums_kernel(
-    const float* __restrict__ logits, const float* __restrict__ q, const float* __restrict__ row_max,
-    const float* __restrict__ row_sum, const int32_t* __restrict__ n_accepted, int gamma, int V,
-    int NC, double* __restrict__ csum, double* __restrict__ psum) {
-    // flat grid: workgroup x covers chunk x % NC of sequence x / NC
-    const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
-    const DrawRow d = draw_row(logits, q, row_max, row_sum, n_accepted, b, gamma, V);
-    float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights16(d, c * kDrawChunk + threadIdx.x * kDrawPerThread, w, p);
-    double tw = 0.0, tp = 0.0;
-#pragma unroll
-    for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
-    double tot_w, tot_p;
-    block_inclusive_scan(tw, &tot_w);
-    block_inclusive_scan(tp, &tot_p);
-    if (threadIdx.x == 0) {
-        csum[(size_t)b * NC + c] = tot_w;
-        psum[(size_t)b * NC + c] = tot_p;
-    }
-}
-
-// Exclusive prefix of one double per thread: the inclusive value of the
-// previous thread, so that excl(t) + own(t) is never needed.
-__device__ double block_exclusive_scan(double v, double* total) {
-    __shared__ double s_last[kBlock / kWave];
-    const double incl = block_inclusive_scan(v, total);
-    const int lane = threadIdx.x & (kWave - 1);
-    const double up = __shfl_up(incl, 1);
-    if (lane == kWave - 1) s_last[threadIdx.x / kWave] = incl;
-    __syncthreads();
-    const double r = lane > 0 ? up : (threadIdx.x == 0 ? 0.0 : s_last[threadIdx.x / kWave - 1]);
-    __syncthreads();
-    return r;
-}
-
-__global__ __launch_bounds__(kBlock) void draw_pick_kernel(
-    const float* __restrict__ logits, const float* __restrict__ q, const float* __restrict__ row_max,
-    const float* __restrict__ row_sum, const int32_t* __restrict__ n_accepted,
-    const float* __restrict__ uniforms, int gamma, int V, int NC, const double* __restrict__ csum,
-    const double* __restrict__ psum, int32_t* __restrict__ out_tokens, int32_t* __restrict__ status) {
+// The inverse-CDF draw for sequence b from its chunk totals.  Returns the
+// token; *flags gets SV_DEV_FALLBACK / SV_DEV_NONFINITE.
+__device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* psum, float u,
+                    int* flags) {
     __shared__ double s_before;
-    const int b = blockIdx.x;
-    DrawRow d = draw_row(logits, q, row_max, row_sum, n_accepted, b, gamma, V);
-    const int n = n_accepted[b];
-    const size_t out_at = (size_t)b * (gamma + 1) + n;
     // Thread t owns chunks [t*per, (t+1)*per) of the chunk totals.
     const int per = (NC + kBlock - 1) / kBlock;
     const int c0 = threadIdx.x * per, c1 = min(NC, c0 + per);
@@ -239,9 +238,9 @@ __global__ __launch_bounds__(kBlock) void draw_pick_kernel(
     double own = 0.0, S;
     for (int c = c0; c < c1; ++c) own += sums[c];
     double excl = block_exclusive_scan(own, &S);
-    int flags = 0;
+    *flags = 0;
     if (!(S > 0.0)) {
-        flags = SV_DEV_FALLBACK;
+        *flags = SV_DEV_FALLBACK;
         d.qrow = nullptr;
         sums = psum + (size_t)b * NC;
         own = 0.0;
@@ -249,13 +248,10 @@ __global__ __launch_bounds__(kBlock) void draw_pick_kernel(
         excl = block_exclusive_scan(own, &S);
     }
     if (!(S > 0.0) || !(S < INFINITY)) {
-        if (threadIdx.x == 0) {
-            out_tokens[out_at] = 0;
-            status[b] |= flags | SV_DEV_NONFINITE;
-        }
-        return;
+        *flags |= SV_DEV_NONFINITE;
+        return 0;
     }
-    const double t = (double)uniforms[(size_t)b * (gamma + 1) + gamma] * S;
+    const double t = (double)u * S;
 
     // The first chunk whose running sum reaches t and that carries weight;
     // failing that (only through rounding), the last chunk with weight.
@@ -270,8 +266,7 @@ __global__ __launch_bounds__(kBlock) void draw_pick_kernel(
     }
     int chunk = block_min_int(first);
     if (chunk == INT_MAX) chunk = block_max_int(last_pos);
-    // Running sum before that chunk, from its owner, in the same order.
-    if (c0 <= chunk && chunk < c1) {
+    if (c0 <= chunk && chunk < c1) {          // its owner: running sum before it, same order
         double r = excl;
         for (int c = c0; c < chunk; ++c) r += sums[c];
         s_before = r;
@@ -279,8 +274,7 @@ __global__ __launch_bounds__(kBlock) void draw_pick_kernel(
     __syncthreads();
     const double before = s_before;
 
-    // Rescan the chunk in token order: exclusive prefix of this thread's
-    // 16 tokens, then their sequential sums.
+    // Rescan that chunk in token order.
     const int j0 = chunk * kDrawChunk + threadIdx.x * kDrawPerThread;
     float w[kDrawPerThread], p[kDrawPerThread];
     draw_weights16(d, j0, w, p);
@@ -298,37 +292,82 @@ __global__ __launch_bounds__(kBlock) void draw_pick_kernel(
             if (y == INT_MAX && base + part >= t) y = j0 + e;
         }
     }
-    int pick = block_min_int(y);
-    if (pick == INT_MAX) pick = block_max_int(ylast);
+    int tok = block_min_int(y);
+    if (tok == INT_MAX) tok = block_max_int(ylast);
+    return tok;
+}
+
+__global__ __launch_bounds__(kBlock) void draw_kernel(
+    const float* __restrict__ logits, const float* __restrict__ part_max,
+    const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
+    const float* __restrict__ q, const float* __restrict__ uniforms, int gamma, int V, int NC,
+    double* __restrict__ csum, double* __restrict__ psum, int32_t* __restrict__ counters,
+    float* __restrict__ row_max, float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
+    __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
+    __shared__ int s_last;
+    // flat grid: workgroup x covers chunk x % NC of sequence x / NC
+    const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
+    const int g1 = gamma + 1;
+
+    bool bad;
+    const int n = accept_tests(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q, uniforms,
+                               r_m, r_s, &bad);
+    const size_t k = (size_t)b * g1 + n;
+    DrawRow d;
+    d.lrow = logits + k * V;
+    d.qrow = n < gamma ? q + ((size_t)b * gamma + n) * V : nullptr;
+    d.M = r_m[n];
+    d.S = r_s[n];
+    d.V = V;
+
+    float w[kDrawPerThread], p[kDrawPerThread];
+    draw_weights16(d, c * kDrawChunk + threadIdx.x * kDrawPerThread, w, p);
+    double tw = 0.0, tp = 0.0;
+#pragma unroll
+    for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
+    double tot_w, tot_p;
+    block_inclusive_scan(tw, &tot_w);
+    block_inclusive_scan(tp, &tot_p);
     if (threadIdx.x == 0) {
-        out_tokens[out_at] = pick;
-        if (flags) status[b] |= flags;
+        csum[(size_t)b * NC + c] = tot_w;
+        psum[(size_t)b * NC + c] = tot_p;
+        __threadfence();                       // publish the totals before counting
+        s_last = atomicAdd(&counters[b], 1) == NC - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();                           // see every other chunk's totals
+
+    // The sequence's last workgroup: outputs that depend on n only ...
+    if (threadIdx.x < g1) {
+        const int i = threadIdx.x;
+        row_max[(size_t)b * g1 + i] = r_m[i];
+        row_sum[(size_t)b * g1 + i] = r_s[i];
+        if (i != n) out_tokens[(size_t)b * g1 + i] = i < n ? draft[(size_t)b * gamma + i] : -1;
+    }
+    // ... and the draw.
+    int flags;
+    const int tok = pick(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], &flags);
+    if (threadIdx.x == 0) {
+        out_tokens[k] = tok;
+        n_accepted[b] = n;
+        status[b] = (bad ? SV_DEV_BAD_DRAFT : 0) | flags;
+        counters[b] = 0;                       // ready for a repeated stage-2 call
     }
 }
 
 }  // namespace
 
-hipError_t launch_accept(const float* logits, const float* part_max, const float* part_sum, int NP,
-                         int B, int gamma, int V, const int32_t* draft, const float* q,
-                         const float* uniforms, float* row_max, float* row_sum, int32_t* out_tokens,
-                         int32_t* n_accepted, int32_t* status, hipStream_t stream) {
-    accept_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(logits, part_max, part_sum, NP, gamma, V, draft, q,
-                                                       uniforms, row_max, row_sum, out_tokens,
-                                                       n_accepted, status);
-    return hipGetLastError();
-}
-
-hipError_t launch_draw(const float* logits, const float* q, const float* row_max, const float* row_sum,
-                       const int32_t* n_accepted, const float* uniforms, int B, int gamma, int V,
-                       int NC, double* csum, double* psum, int32_t* out_tokens, int32_t* status,
-                       hipStream_t stream) {
-    draw_sums_kernel<<<dim3((unsigned)NC * (unsigned)B), dim3(kBlock), 0, stream>>>(logits, q, row_max, row_sum, n_accepted,
-                                                             gamma, V, NC, csum, psum);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    draw_pick_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(logits, q, row_max, row_sum, n_accepted,
-                                                          uniforms, gamma, V, NC, csum, psum,
-                                                          out_tokens, status);
+hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
+                              int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
+                              const float* q, const float* uniforms, int NC, double* csum,
+                              double* psum, int32_t* counters, float* row_max, float* row_sum,
+                              int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
+                              hipStream_t stream) {
+    draw_kernel<<<dim3((unsigned)NC * (unsigned)B), dim3(kBlock), 0, stream>>>(
+        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum, counters,
+        row_max, row_sum, out_tokens, n_accepted, status);
     return hipGetLastError();
 }
 

@@ -5,16 +5,16 @@
 #include "sv_common.h"
 
 namespace sv {
+int lmhead_grid(int V);
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                         float* logits, float* part_max, float* part_sum, int NP, hipStream_t stream);
-hipError_t launch_accept(const float* logits, const float* part_max, const float* part_sum, int NP,
-                         int B, int gamma, int V, const int32_t* draft, const float* q,
-                         const float* uniforms, float* row_max, float* row_sum, int32_t* out_tokens,
-                         int32_t* n_accepted, int32_t* status, hipStream_t stream);
-hipError_t launch_draw(const float* logits, const float* q, const float* row_max, const float* row_sum,
-                       const int32_t* n_accepted, const float* uniforms, int B, int gamma, int V,
-                       int NC, double* csum, double* psum, int32_t* out_tokens, int32_t* status,
-                       hipStream_t stream);
+                         float* logits, float* part_max, float* part_sum, int NPs, int grid,
+                         int32_t* counters, int n_counters, hipStream_t stream);
+hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
+                              int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
+                              const float* q, const float* uniforms, int NC, double* csum,
+                              double* psum, int32_t* counters, float* row_max, float* row_sum,
+                              int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
+                              hipStream_t stream);
 }  // namespace sv
 
 namespace {
@@ -43,23 +43,20 @@ sv_status check_workspace(const void* ws, size_t bytes, sv_dims dims) {
 sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* ws, hipStream_t s) {
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     hipError_t e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
-                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NP, s);
+                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NPs,
+                                     sv::lmhead_grid(dims.V), at<int32_t>(ws, L.counters), dims.B, s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
 sv_status stage2(const int32_t* draft, const float* q, const float* uniforms, sv_dims dims,
                  int32_t* out_tokens, int32_t* n_accepted, void* ws, hipStream_t s) {
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
-    hipError_t e = sv::launch_accept(at<float>(ws, L.logits), at<float>(ws, L.part_max),
-                                     at<float>(ws, L.part_sum), L.NP, dims.B, dims.gamma, dims.V,
-                                     draft, q, uniforms, at<float>(ws, L.row_max),
-                                     at<float>(ws, L.row_sum), out_tokens, n_accepted,
-                                     at<int32_t>(ws, L.status), s);
-    if (e != hipSuccess) return SV_ERR_DEVICE;
-    e = sv::launch_draw(at<float>(ws, L.logits), q, at<float>(ws, L.row_max), at<float>(ws, L.row_sum),
-                        n_accepted, uniforms, dims.B, dims.gamma, dims.V, L.NC,
-                        at<double>(ws, L.csum), at<double>(ws, L.psum), out_tokens,
-                        at<int32_t>(ws, L.status), s);
+    hipError_t e = sv::launch_accept_draw(
+        at<float>(ws, L.logits), at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
+        sv::lmhead_grid(dims.V), L.NPs, dims.B, dims.gamma, dims.V, draft, q, uniforms, L.NC,
+        at<double>(ws, L.csum), at<double>(ws, L.psum), at<int32_t>(ws, L.counters),
+        at<float>(ws, L.row_max), at<float>(ws, L.row_sum), out_tokens, n_accepted,
+        at<int32_t>(ws, L.status), s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 

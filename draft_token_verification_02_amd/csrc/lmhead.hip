@@ -1,5 +1,5 @@
 // LM-head GEMM of the verification step: logits = hidden . W^T for all
-// B*(gamma+1) rows in one pass over W, plus per-tile softmax partials.
+// B*(gamma+1) rows in one pass over W, plus per-workgroup softmax partials.
 //
 // Source: "推测解码" (world.lapla.si/zh/specdec), section 先让小模型猜 -- the
 // target scores every drafted position plus one in a single read of its
@@ -11,169 +11,271 @@
 // streaming W from HBM.  Each W byte is loaded exactly once, straight into
 // the A operand of v_mfma_f32_16x16x32_bf16 (16 vocab rows x 32 k per
 // fragment, 16 contiguous bytes per lane); the hidden rows are the B operand
-// (16 rows x 32 k), re-read from L2 once per fragment step and shared by the
-// wave's four vocab fragments.  K is a pure reduction, so both operands use
-// the same (lane group, element) -> k mapping and no reordering is needed.
+// (16 rows x 32 k), re-read from L2 and shared by the T vocab fragments a
+// wave works on at once.  K is a pure reduction, so both operands use the
+// same (lane group, element) -> k mapping and no reordering is needed.
 //
-// Each wave owns 64 vocab rows for the full K range, so there is no barrier
-// in the main loop.  Loads run one stage (2 k-steps x 4 fragments = 8 KB per
-// wave) ahead of the MFMAs.  The epilogue stores the fp32 logits and reduces
-// each row's 256-entry workgroup slice to a (max, sum exp) partial for the
-// softmax, so no later pass needs to re-read the logits to normalise them.
+// Launch shape.  The grid is persistent: one workgroup of kLmWaves waves per
+// compute unit (the register budget lets only one fit), and the vocabulary's
+// groups of T fragments are split evenly over all waves.  Each wave streams
+// its contiguous range as one sequence of (group, k-step) loads kept U steps
+// ahead of the MFMAs in a register ring; the ring runs across group
+// boundaries, so a group's epilogue (the fp32 logit stores and a running
+// (max, sum exp) per row) overlaps the next group's loads.  Few rows per
+// wave with a deep ring keeps each wave's HBM accesses on few DRAM pages.
+// The workgroup reduces its running maxima and sums to one softmax partial
+// per row, so no later pass has to re-read the logits to normalise them.
 
 #include "sv_common.h"
+
+#ifndef SV_LM_WG_PER_CU
+#define SV_LM_WG_PER_CU 1
+#endif
+// Fragments of 16 vocab rows per wave the grid aims at; 0 = persistent (one
+// workgroup per CU, the vocabulary split over them).
+#ifndef SV_LM_TILES_PER_WAVE
+#define SV_LM_TILES_PER_WAVE 0
+#endif
 
 namespace sv {
 
 namespace {
 
-constexpr int T = kLmTilesPerWave;
-constexpr int U = 2;                 // k-steps (of 32) per pipeline stage
+// Fragments per wave and ring depth (k-steps in flight) by hidden-row
+// fragments MT, from a sweep on MI355X at d = 1536 and 4096: four fragments
+// four steps deep for one hidden fragment; more fragments, to share each
+// hidden-row load, and shallower rings as MT grows.
+#ifndef SV_LM1_T
+#define SV_LM1_T 4
+#endif
+#ifndef SV_LM1_U
+#define SV_LM1_U 4
+#endif
+#ifndef SV_LM2_T
+#define SV_LM2_T 4
+#endif
+#ifndef SV_LM2_U
+#define SV_LM2_U 2
+#endif
+#ifndef SV_LM3_T
+#define SV_LM3_T 8
+#endif
+#ifndef SV_LM3_U
+#define SV_LM3_U 2
+#endif
+#ifndef SV_LM4_T
+#define SV_LM4_T 4
+#endif
+#ifndef SV_LM4_U
+#define SV_LM4_U 2
+#endif
+template <int MT> struct LmCfg;
+template <> struct LmCfg<1> { static constexpr int T = SV_LM1_T, U = SV_LM1_U; };
+template <> struct LmCfg<2> { static constexpr int T = SV_LM2_T, U = SV_LM2_U; };
+template <> struct LmCfg<3> { static constexpr int T = SV_LM3_T, U = SV_LM3_U; };
+template <> struct LmCfg<4> { static constexpr int T = SV_LM4_T, U = SV_LM4_U; };
+constexpr int kGenericU = 4;         // ring depth of the path for ragged d
 
-template <int MT>
-struct Frags {
-    uint4 w[U][T];
-    uint4 h[U][MT];
-};
+template <int MT, int T, int U, bool FAST>
+__global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int row0, int rows,
+    int d, int V, float* __restrict__ logits, float* __restrict__ part_max,
+    float* __restrict__ part_sum, int NPs, int32_t* __restrict__ counters, int n_counters) {
+    const int lane = threadIdx.x & (kWave - 1);
+    // The wave index is the same on every lane; saying so keeps the wave's
+    // range, cursors and branches in scalar registers, which lets the
+    // compiler keep the load ring in flight across loop iterations.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15;      // fragment row this lane loads (A: vocab, B: hidden)
+    const int kg = lane >> 4;       // 8-element k group of this lane
 
-template <int MT>
-__device__ __forceinline__ void load_stage(Frags<MT>& f, const uint4* const (&wp)[T],
-                                           const uint4* const (&hp)[MT], int step) {
+    // The draw stage counts finished workgroups per sequence; start it at zero.
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
+        counters[i] = 0;
+
+    // This wave's groups of T fragments: an even split of all groups.
+    const int ntiles = (V + kLmTile - 1) / kLmTile;
+    const int ngroups = (ntiles + T - 1) / T;
+    const int nwaves = gridDim.x * kLmWaves;
+    const int wid = blockIdx.x * kLmWaves + wave;
+    const int base = ngroups / nwaves, extra = ngroups % nwaves;
+    const int gb = wid * base + min(wid, extra);
+    const int ge = gb + base + (wid < extra ? 1 : 0);
+    const int nstep = (d + 31) / 32;
+
+    const u32x4* hp[MT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int off = (step + u) * 4;   // 32 bf16 = 4 uint4 per k-step
-#pragma unroll
-        for (int t = 0; t < T; ++t) f.w[u][t] = wp[t][off];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) f.h[u][m] = hp[m][off];
+    for (int m = 0; m < MT; ++m) {
+        const int r = row0 + min(m * kLmTile + r16, rows - 1);   // pad rows repeat the last row
+        hp[m] = reinterpret_cast<const u32x4*>(hidden + (size_t)r * d) + kg;
     }
-}
 
-template <int MT>
-__device__ __forceinline__ void mma_stage(const Frags<MT>& f, f32x4 (&acc)[T][MT]) {
+    // Load cursor (group lg, k-step lk) with its fragment row pointers.
+    // Rows past V are clamped to a valid row; their results are never kept.
+    int lg = gb, lk = 0;
+    const u32x4* lp[T];
+    auto set_rows = [&](int g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int t = 0; t < T; ++t) {
+            const int v = min((g * T + t) * kLmTile + r16, V - 1);
+            lp[t] = reinterpret_cast<const u32x4*>(W + (size_t)v * d) + kg;
+        }
+    };
+    set_rows(lg);
+    u32x4 wr[U][T], hr[U][MT];
+    auto load = [&](int slot) {
+        if (FAST || lk * 32 + kg * 8 < d) {        // lanes past d load nothing
+#pragma unroll
+            for (int t = 0; t < T; ++t) wr[slot][t] = lp[t][lk * 4];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) hr[slot][m] = hp[m][lk * 4];
+        } else {
+#pragma unroll
+            for (int t = 0; t < T; ++t) wr[slot][t] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int m = 0; m < MT; ++m) hr[slot][m] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto advance = [&]() {
+        if (++lk == nstep) { lk = 0; ++lg; if (lg < ge) set_rows(lg); }
+    };
+
+    f32x4 acc[T][MT];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto mma = [&](int slot) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, f.w[u][t]), __builtin_bit_cast(bf16x8, f.h[u][m]),
+                    __builtin_bit_cast(bf16x8, wr[slot][t]), __builtin_bit_cast(bf16x8, hr[slot][m]),
                     acc[t][m], 0, 0, 0);
-}
+    };
 
-// One k-step of 32 with the k range cut at d (d is a multiple of 8, so each
-// lane's 8-element group is either wholly inside or wholly outside).
-template <int MT>
-__device__ __forceinline__ void masked_step(const uint4* const (&wp)[T], const uint4* const (&hp)[MT],
-                                            int step, int kg, int d, f32x4 (&acc)[T][MT]) {
-    const bool in = step * 32 + kg * 8 < d;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    uint4 w[T], h[MT];
+    // Running softmax partial of this lane's hidden rows over its vocab entries.
+    float run_m[MT], run_s[MT];
 #pragma unroll
-    for (int t = 0; t < T; ++t) w[t] = in ? wp[t][step * 4] : zero;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) h[m] = in ? hp[m][step * 4] : zero;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, w[t]), __builtin_bit_cast(bf16x8, h[m]), acc[t][m], 0, 0, 0);
-}
-
-template <int MT>
-__global__ __launch_bounds__(kBlock) void lmhead_kernel(
-    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int row0, int rows,
-    int d, int V, float* __restrict__ logits, float* __restrict__ part_max,
-    float* __restrict__ part_sum, int NP) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int r16 = lane & 15;      // fragment row this lane loads (A: vocab, B: hidden)
-    const int kg = lane >> 4;       // 8-element k group of this lane
-    const int v_wave = blockIdx.x * kLmVocabPerBlock + wave * (T * kLmTile);
-
-    // Per-lane fragment row pointers; rows past the end are clamped to a valid
-    // row and their results are never stored.
-    const uint4* wp[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int v = min(v_wave + t * kLmTile + r16, V - 1);
-        wp[t] = reinterpret_cast<const uint4*>(W + (size_t)v * d) + kg;
-    }
-    const uint4* hp[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int r = row0 + min(m * kLmTile + r16, rows - 1);
-        hp[m] = reinterpret_cast<const uint4*>(hidden + (size_t)r * d) + kg;
-    }
-
-    f32x4 acc[T][MT];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Full stages of U k-steps, ping-pong between two register buffers.
-    const int nstage = d / (32 * U);
-    if (nstage > 0) {
-        Frags<MT> fa, fb;
-        load_stage<MT>(fa, wp, hp, 0);
-        for (int s = 0; s < nstage; s += 2) {
-            if (s + 1 < nstage) load_stage<MT>(fb, wp, hp, (s + 1) * U);
-            mma_stage<MT>(fa, acc);
-            if (s + 2 < nstage) load_stage<MT>(fa, wp, hp, (s + 2) * U);
-            if (s + 1 < nstage) mma_stage<MT>(fb, acc);
-        }
-    }
-    // Remaining k-steps (d not a multiple of 64), each cut at d.
-    const int nstep = (d + 31) / 32;
-    for (int step = nstage * U; step < nstep; ++step) masked_step<MT>(wp, hp, step, kg, d, acc);
-
-    // Epilogue.  Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment.
-    __shared__ float s_max[kBlock / kWave][MT * kLmTile];
-    __shared__ float s_sum[kBlock / kWave][MT * kLmTile];
+    for (int m = 0; m < MT; ++m) { run_m[m] = -INFINITY; run_s[m] = 0.f; }
     const bool vec_store = (V & 3) == 0;
+    // Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment.
+    auto epilogue = [&](int g) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int rr = m * kLmTile + r16;                // row within this pass
-        const bool row_ok = rr < rows;
-        float* lrow = logits + (size_t)(row0 + (row_ok ? rr : 0)) * V;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int v = v_wave + t * kLmTile + kg * 4;
-            if (row_ok) {
-                if (vec_store) {
-                    if (v < V) *reinterpret_cast<float4*>(lrow + v) =
-                        make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (v + i < V) lrow[v + i] = acc[t][m][i];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (v + i < V) mx = fmaxf(mx, acc[t][m][i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        float sm = 0.f;
-        if (mx != -INFINITY) {
+        for (int m = 0; m < MT; ++m) {
+            const int rr = m * kLmTile + r16;
+            const bool row_ok = rr < rows;
+            float* lrow = logits + (size_t)(row0 + (row_ok ? rr : 0)) * V;
+            float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const int v = v_wave + t * kLmTile + kg * 4;
+                const int v = (g * T + t) * kLmTile + kg * 4;
+                if (row_ok) {
+                    if (vec_store) {
+                        if (v < V) *reinterpret_cast<float4*>(lrow + v) =
+                            make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (v + i < V) lrow[v + i] = acc[t][m][i];
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (v + i < V) sm += expf(acc[t][m][i] - mx);
+                    if (v + i < V) mx = fmaxf(mx, acc[t][m][i]);
+            }
+            if (mx != -INFINITY) {
+                const float nm = fmaxf(run_m[m], mx);
+                float sm = run_s[m] * expf(run_m[m] - nm);   // exp(-inf) = 0 the first time
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int v = (g * T + t) * kLmTile + kg * 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (v + i < V) sm += expf(acc[t][m][i] - nm);
+                }
+                run_m[m] = nm;
+                run_s[m] = sm;
             }
         }
-        sm += __shfl_xor(sm, 16);
-        sm += __shfl_xor(sm, 32);
+    };
+
+    // Fill the ring, then stream: MFMA on the oldest slot, refill it.
+    zero_acc();
+    int cg = gb, ck = 0;
+    if (gb < ge) {
+        if (FAST) {
+            // nstep is a multiple of U, so groups start and end on ring
+            // boundaries and the load cursor moves once per block.  The
+            // block's loads are unconditional: past the wave's last group the
+            // cursor keeps pointing at that group's rows (valid memory; the
+            // loaded values are never used), which keeps the loop free of
+            // branches around loads and the loads in flight across iterations.
+            auto load_block = [&]() {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int t = 0; t < T; ++t) wr[u][t] = lp[t][(lk + u) * 4];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) hr[u][m] = hp[m][(lk + u) * 4];
+                }
+            };
+            auto next_block = [&]() {
+                lk += U;
+                if (lk == nstep) { lk = 0; ++lg; if (lg < ge) set_rows(lg); }
+            };
+            load_block();
+            next_block();
+            while (cg < ge) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    mma(u);
+#pragma unroll
+                    for (int t = 0; t < T; ++t) wr[u][t] = lp[t][(lk + u) * 4];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) hr[u][m] = hp[m][(lk + u) * 4];
+                }
+                next_block();
+                ck += U;
+                if (ck == nstep) { epilogue(cg); zero_acc(); ck = 0; ++cg; }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (lg < ge) load(u);
+                advance();
+            }
+            while (cg < ge) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (cg < ge) {
+                        mma(u);
+                        if (lg < ge) load(u);
+                        advance();
+                        if (++ck == nstep) { epilogue(cg); zero_acc(); ck = 0; ++cg; }
+                    }
+                }
+            }
+        }
+    }
+
+    // One partial per hidden row for the whole workgroup.
+    __shared__ float s_max[kLmWaves][MT * kLmTile];
+    __shared__ float s_sum[kLmWaves][MT * kLmTile];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float mm = run_m[m], ss = run_s[m];
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) {
+            const float m2 = __shfl_xor(mm, off), s2 = __shfl_xor(ss, off);
+            lse_merge(mm, ss, m2, s2);
+        }
         if (kg == 0) {
-            s_max[wave][rr] = mx;
-            s_sum[wave][rr] = sm;
+            s_max[wave][m * kLmTile + r16] = mm;
+            s_sum[wave][m * kLmTile + r16] = ss;
         }
     }
     __syncthreads();
@@ -181,27 +283,65 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(
         const int rr = threadIdx.x;
         float m = -INFINITY, s = 0.f;
 #pragma unroll
-        for (int w = 0; w < kBlock / kWave; ++w) lse_merge(m, s, s_max[w][rr], s_sum[w][rr]);
-        part_max[(size_t)(row0 + rr) * NP + blockIdx.x] = m;
-        part_sum[(size_t)(row0 + rr) * NP + blockIdx.x] = s;
+        for (int w = 0; w < kLmWaves; ++w) lse_merge(m, s, s_max[w][rr], s_sum[w][rr]);
+        part_max[(size_t)(row0 + rr) * NPs + blockIdx.x] = m;
+        part_sum[(size_t)(row0 + rr) * NPs + blockIdx.x] = s;
     }
+}
+
+int cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    int* slot = dev >= 0 && dev < 64 ? &cached[dev] : nullptr;
+    int n = slot ? __atomic_load_n(slot, __ATOMIC_RELAXED) : 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        if (slot) __atomic_store_n(slot, n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
+template <int MT>
+void launch_mt(dim3 g, dim3 b, hipStream_t s, const uint16_t* hidden, const uint16_t* W, int row0,
+               int rows, int d, int V, float* logits, float* pm, float* ps, int NPs,
+               int32_t* counters, int nc) {
+    constexpr int T = LmCfg<MT>::T, U = LmCfg<MT>::U;
+    const int nstep = (d + 31) / 32;
+    if (d % 32 == 0 && nstep % U == 0)
+        lmhead_kernel<MT, T, U, true><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, NPs, counters, nc);
+    else
+        lmhead_kernel<MT, T, kGenericU, false><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, NPs, counters, nc);
 }
 
 }  // namespace
 
+// Workgroups of the LM-head launch (also the number of softmax partials per
+// row): one per compute unit, capped so every wave has fragments to stream.
+int lmhead_grid(int V) {
+    if (SV_LM_TILES_PER_WAVE > 0) {
+        const int ntiles = (V + kLmTile - 1) / kLmTile;
+        const int per_wg = SV_LM_TILES_PER_WAVE * kLmWaves;
+        return max(1, min((ntiles + per_wg - 1) / per_wg, lmhead_useful_groups(V)));
+    }
+    return max(1, min(cu_count() * SV_LM_WG_PER_CU, lmhead_useful_groups(V)));
+}
+
 // Enqueue the LM-head stage: one launch per group of up to 64 hidden rows.
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                         float* logits, float* part_max, float* part_sum, int NP,
-                         hipStream_t stream) {
+                         float* logits, float* part_max, float* part_sum, int NPs, int grid,
+                         int32_t* counters, int n_counters, hipStream_t stream) {
     for (int row0 = 0; row0 < R; row0 += kLmRowsPerPass) {
         const int rows = min(kLmRowsPerPass, R - row0);
         const int mt = (rows + kLmTile - 1) / kLmTile;
-        dim3 grid(NP), block(kBlock);
+        const int nc = row0 == 0 ? n_counters : 0;
+        dim3 g(grid), b(kLmWaves * kWave);
         switch (mt) {
-            case 1: lmhead_kernel<1><<<grid, block, 0, stream>>>(hidden, W, row0, rows, d, V, logits, part_max, part_sum, NP); break;
-            case 2: lmhead_kernel<2><<<grid, block, 0, stream>>>(hidden, W, row0, rows, d, V, logits, part_max, part_sum, NP); break;
-            case 3: lmhead_kernel<3><<<grid, block, 0, stream>>>(hidden, W, row0, rows, d, V, logits, part_max, part_sum, NP); break;
-            default: lmhead_kernel<4><<<grid, block, 0, stream>>>(hidden, W, row0, rows, d, V, logits, part_max, part_sum, NP); break;
+            case 1: launch_mt<1>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
+            case 2: launch_mt<2>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
+            case 3: launch_mt<3>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
+            default: launch_mt<4>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

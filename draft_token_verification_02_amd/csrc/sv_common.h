@@ -12,20 +12,35 @@ namespace sv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes = 8 bf16
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;              // threads per workgroup of every kernel
+constexpr int kBlock = 256;              // threads per workgroup of the draw kernel
+
 constexpr int kLmTile = 16;              // vocab rows (and hidden rows) per MFMA fragment
-constexpr int kLmTilesPerWave = 4;       // vocab fragments per wave in the LM-head kernel
-constexpr int kLmVocabPerBlock = (kBlock / kWave) * kLmTilesPerWave * kLmTile;  // 256
+#ifndef SV_LM_WAVES
+#define SV_LM_WAVES 4
+#endif
+constexpr int kLmWaves = SV_LM_WAVES;    // waves per LM-head workgroup
+constexpr int kLmMaxPartials = 1024;     // LM-head workgroups (softmax partials per row), at most
 constexpr int kLmRowsPerPass = 64;       // hidden rows one LM-head launch handles
-constexpr int kDrawPerThread = 16;       // vocab entries per thread in the draw kernels
+constexpr int kDrawPerThread = 16;       // vocab entries per thread in the draw kernel
 constexpr int kDrawChunk = kBlock * kDrawPerThread;                             // 4096
 
-// Byte offsets of every array inside the caller's workspace.
+// LM-head workgroups worth launching for a vocabulary of V: at least one
+// 16-row fragment per wave.
+static inline int lmhead_useful_groups(int V) {
+    const int ntiles = (V + kLmTile - 1) / kLmTile;
+    const int g = (ntiles + kLmWaves - 1) / kLmWaves;
+    return g < kLmMaxPartials ? g : kLmMaxPartials;
+}
+
+// Byte offsets of every array inside the caller's workspace.  The partial
+// arrays have a row stride NPs (a multiple of 4, for 16-byte loads) that
+// bounds the LM-head grid on any device.
 struct Layout {
-    int R, NP, NC;
-    size_t logits, part_max, part_sum, row_max, row_sum, status, csum, psum, total;
+    int R, NPs, NC;
+    size_t logits, part_max, part_sum, row_max, row_sum, status, counters, csum, psum, total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -34,15 +49,16 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     (void)d;
     Layout L;
     L.R = B * (gamma + 1);
-    L.NP = (V + kLmVocabPerBlock - 1) / kLmVocabPerBlock;
+    L.NPs = (lmhead_useful_groups(V) + 3) / 4 * 4;
     L.NC = (V + kDrawChunk - 1) / kDrawChunk;
     size_t off = 0;
     L.logits = off;   off = align_up(off + (size_t)L.R * V * sizeof(float), 256);
-    L.part_max = off; off = align_up(off + (size_t)L.R * L.NP * sizeof(float), 256);
-    L.part_sum = off; off = align_up(off + (size_t)L.R * L.NP * sizeof(float), 256);
+    L.part_max = off; off = align_up(off + (size_t)L.R * L.NPs * sizeof(float), 256);
+    L.part_sum = off; off = align_up(off + (size_t)L.R * L.NPs * sizeof(float), 256);
     L.row_max = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
     L.row_sum = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
     L.status = off;   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
+    L.counters = off; off = align_up(off + (size_t)B * sizeof(int32_t), 256);
     L.csum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
     L.psum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
     L.total = off;
@@ -50,6 +66,7 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
 }
 
 // Merge of two (max, sum of exp(x - max)) pairs: the online-softmax step.
+// Symmetric in its two arguments, so a butterfly gives every lane the same bits.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
     if (m2 == -INFINITY) return;
     if (m == -INFINITY) { m = m2; s = s2; return; }

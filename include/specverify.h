@@ -112,8 +112,9 @@ SV_API sv_status sv_lmhead(const uint16_t *hidden, const uint16_t *W_lmhead, sv_
                     void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Stage 2 alone: softmax normalisers, accept tests, first rejection and the
- * replacement/bonus draw, from the logits stage 1 left in the same
- * workspace with the same dims.  (Steps 2-6 above.) */
+ * replacement/bonus draw, from the logits and partials stage 1 left in the
+ * same workspace, with the same dims, on the same device (stage 1 also
+ * resets the per-sequence counters stage 2 uses).  (Steps 2-6 above.) */
 SV_API sv_status sv_accept_and_draw(const int32_t *draft_tokens, const float *q, const float *uniforms,
                              sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
                              void *workspace, size_t workspace_bytes, void *hip_stream);

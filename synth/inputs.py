@@ -274,7 +274,7 @@ def repeated_trials(base: Dict[str, np.ndarray], n: int, seed: int, *,
 
 
 def iid_positions(V: int, d: int, gamma: int, n: int, seed: int, *, sigma: float = 1.0,
-                  w_std: float = 1.0) -> Dict[str, np.ndarray]:
+                  w_std: float = 0.25) -> Dict[str, np.ndarray]:
     """Trials in which every position is equally easy to guess.
 
     All gamma+1 hidden rows are the same vector and all gamma q rows are the
