@@ -8,25 +8,25 @@
 //     later drafts; when every draft passes, emit the target's own token at
 //     the extra position, which the same weight read already scored.
 //
-// One kernel after the LM head, one 256-thread workgroup per (sequence b,
-// 4096-token chunk c).  Every workgroup of a sequence
-//   1. gathers l[x_i], q[x_i] and r_i of the gamma drafts and, meanwhile,
-//      merges each of the sequence's gamma+1 rows' LM-head partials (one per
-//      LM-head workgroup, 16-byte loads, 32 threads per row) into the row's
-//      softmax normaliser;
-//   2. runs the gamma accept tests r * q <= p and takes n, the number of
+// After the LM head, one 256-thread workgroup per (sequence b, 4096-token
+// chunk c) of draw_kernel.  For sequence b they
+//   1. gather l[x_i], q[x_i] and r_i of the gamma drafts and, meanwhile,
+//      merge each of the sequence's gamma+1 rows' LM-head partials (16-byte
+//      loads, 32 threads per row) into the row's softmax normaliser;
+//   2. run the gamma accept tests r * q <= p and take n, the number of
 //      leading accepts, from a wave ballot;
-//   3. computes fp64 totals of its chunk's draw weights -- the residual
+//   3. compute fp64 totals of the chunk's draw weights -- the residual
 //      max(0, p - q) at row n, or p at row gamma for the bonus -- and of p.
 // The last workgroup of the sequence to finish (a per-sequence counter that
-// the LM-head launch zeroes) writes n, the kept drafts, the padding and the
-// status, scans the chunk totals, finds the chunk where the running sum
-// reaches u * S, rescans that chunk with the same code and picks the first
-// token that reaches it: an inverse CDF over ascending token ids.
+// the LM-head launch zeroes) scans the chunk totals, finds the chunk where
+// the running sum reaches u * S, rescans that chunk with the same code and
+// picks the first token that reaches it: an inverse CDF over ascending ids.
 //
-// Steps 1-2 are repeated by every chunk workgroup of a sequence; they read
-// (gamma+1) * NP * 8 bytes of partials, far less than the chunk itself, and
-// spare a kernel boundary between the accept test and the draw.
+// Steps 1-2 run in one of two places.  With few draw workgroups every chunk
+// workgroup repeats them (they read (gamma+1) * NP * 8 bytes, little next to
+// the chunk) and the step needs no extra kernel boundary.  With many,
+// accept_kernel runs them once per sequence first and the chunk workgroups
+// read n and the draw row's normaliser from memory.
 
 #include "sv_common.h"
 
@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kRowThreads = 32;                  // threads merging one row's partials
 constexpr int kRowsPerPass = kBlock / kRowThreads;
-constexpr int kMergeLoads = kLmMaxPartials / 4 / kRowThreads;   // float4 loads per thread per row
+constexpr int kMergeLoads = 2;                   // float4 loads per thread per row and batch
 
 __device__ __forceinline__ float target_prob(float logit, float row_max, float row_sum) {
     return expf(logit - row_max) / row_sum;
@@ -121,8 +121,9 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
         }
     }
 
-    // 32 threads per row, 8 rows per pass; each thread holds at most
-    // kMergeLoads float4 of maxima and of sums, all loaded before use.
+    // 32 threads per row, 8 rows per pass.  A batch is kMergeLoads float4 of
+    // maxima and of sums per thread (256 partials per row), loaded before
+    // use; the persistent LM-head grid (one workgroup per CU) fits in one.
     const int sub = threadIdx.x % kRowThreads;
     const int grp = threadIdx.x / kRowThreads;
     const int n4 = (NP + 3) / 4;
@@ -133,30 +134,35 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
             const size_t r = (size_t)b * g1 + i;
             const float4* pm = reinterpret_cast<const float4*>(part_max + r * NPs);
             const float4* ps = reinterpret_cast<const float4*>(part_sum + r * NPs);
-            float4 a[kMergeLoads], c[kMergeLoads];
-#pragma unroll
-            for (int u = 0; u < kMergeLoads; ++u) {
-                const int jj = sub + u * kRowThreads;
-                a[u] = jj < n4 ? pm[jj] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                c[u] = jj < n4 ? ps[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int u = 0; u < kMergeLoads; ++u) {
-                const int j = 4 * (sub + u * kRowThreads);     // entries past NP are padding
-                if (j + 0 < NP) m = fmaxf(m, a[u].x);
-                if (j + 1 < NP) m = fmaxf(m, a[u].y);
-                if (j + 2 < NP) m = fmaxf(m, a[u].z);
-                if (j + 3 < NP) m = fmaxf(m, a[u].w);
-            }
-            if (m != -INFINITY) {
+            for (int j0 = 0; j0 < n4; j0 += kMergeLoads * kRowThreads) {
+                float4 a[kMergeLoads], c[kMergeLoads];
 #pragma unroll
                 for (int u = 0; u < kMergeLoads; ++u) {
-                    const int j = 4 * (sub + u * kRowThreads);
-                    if (j + 0 < NP && a[u].x != -INFINITY) s += c[u].x * expf(a[u].x - m);
-                    if (j + 1 < NP && a[u].y != -INFINITY) s += c[u].y * expf(a[u].y - m);
-                    if (j + 2 < NP && a[u].z != -INFINITY) s += c[u].z * expf(a[u].z - m);
-                    if (j + 3 < NP && a[u].w != -INFINITY) s += c[u].w * expf(a[u].w - m);
+                    const int jj = j0 + sub + u * kRowThreads;
+                    a[u] = jj < n4 ? pm[jj] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    c[u] = jj < n4 ? ps[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
+                // this batch's max, then its rescaled sum, merged into (m, s)
+                float bm = -INFINITY, bs = 0.f;
+#pragma unroll
+                for (int u = 0; u < kMergeLoads; ++u) {
+                    const int j = 4 * (j0 + sub + u * kRowThreads);   // entries past NP are padding
+                    if (j + 0 < NP) bm = fmaxf(bm, a[u].x);
+                    if (j + 1 < NP) bm = fmaxf(bm, a[u].y);
+                    if (j + 2 < NP) bm = fmaxf(bm, a[u].z);
+                    if (j + 3 < NP) bm = fmaxf(bm, a[u].w);
+                }
+                if (bm != -INFINITY) {
+#pragma unroll
+                    for (int u = 0; u < kMergeLoads; ++u) {
+                        const int j = 4 * (j0 + sub + u * kRowThreads);
+                        if (j + 0 < NP && a[u].x != -INFINITY) bs += c[u].x * expf(a[u].x - bm);
+                        if (j + 1 < NP && a[u].y != -INFINITY) bs += c[u].y * expf(a[u].y - bm);
+                        if (j + 2 < NP && a[u].z != -INFINITY) bs += c[u].z * expf(a[u].z - bm);
+                        if (j + 3 < NP && a[u].w != -INFINITY) bs += c[u].w * expf(a[u].w - bm);
+                    }
+                }
+                lse_merge(m, s, bm, bs);
             }
         }
 #pragma unroll
@@ -297,6 +303,38 @@ __device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* 
     return tok;
 }
 
+// Accept tests once per sequence (the split form, for many sequences):
+// n, the row normalisers, the kept drafts, padding and status.
+__global__ __launch_bounds__(kBlock) void accept_kernel(
+    const float* __restrict__ logits, const float* __restrict__ part_max,
+    const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
+    const float* __restrict__ q, const float* __restrict__ uniforms, int gamma, int V,
+    float* __restrict__ row_max, float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
+    __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
+    const int b = blockIdx.x;
+    const int g1 = gamma + 1;
+    bool bad;
+    const int n = accept_tests(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q, uniforms,
+                               r_m, r_s, &bad);
+    if (threadIdx.x < g1) {
+        const int i = threadIdx.x;
+        row_max[(size_t)b * g1 + i] = r_m[i];
+        row_sum[(size_t)b * g1 + i] = r_s[i];
+        if (i != n) out_tokens[(size_t)b * g1 + i] = i < n ? draft[(size_t)b * gamma + i] : -1;
+    }
+    if (threadIdx.x == 0) {
+        n_accepted[b] = n;
+        status[b] = bad ? SV_DEV_BAD_DRAFT : 0;
+    }
+}
+
+// FUSED: every chunk workgroup runs the accept tests itself and the
+// sequence's last workgroup picks the token (few sequences: one launch).
+// Otherwise accept_kernel ran first, the workgroup reads n and the draw
+// row's normaliser it left, only writes its chunk totals, and pick_kernel
+// follows: the kernel boundary orders the totals before the pick.
+template <bool FUSED>
 __global__ __launch_bounds__(kBlock) void draw_kernel(
     const float* __restrict__ logits, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
@@ -310,15 +348,25 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
     const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
     const int g1 = gamma + 1;
 
-    bool bad;
-    const int n = accept_tests(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q, uniforms,
-                               r_m, r_s, &bad);
+    bool bad = false;
+    int n;
+    float M, S;
+    if (FUSED) {
+        n = accept_tests(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q, uniforms,
+                         r_m, r_s, &bad);
+        M = r_m[n];
+        S = r_s[n];
+    } else {
+        n = n_accepted[b];
+        M = row_max[(size_t)b * g1 + n];
+        S = row_sum[(size_t)b * g1 + n];
+    }
     const size_t k = (size_t)b * g1 + n;
     DrawRow d;
     d.lrow = logits + k * V;
     d.qrow = n < gamma ? q + ((size_t)b * gamma + n) * V : nullptr;
-    d.M = r_m[n];
-    d.S = r_s[n];
+    d.M = M;
+    d.S = S;
     d.V = V;
 
     float w[kDrawPerThread], p[kDrawPerThread];
@@ -332,15 +380,18 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
     if (threadIdx.x == 0) {
         csum[(size_t)b * NC + c] = tot_w;
         psum[(size_t)b * NC + c] = tot_p;
-        __threadfence();                       // publish the totals before counting
-        s_last = atomicAdd(&counters[b], 1) == NC - 1;
+        if (FUSED) {
+            __threadfence();                   // publish the totals before counting
+            s_last = atomicAdd(&counters[b], 1) == NC - 1;
+        }
     }
+    if (!FUSED) return;
     __syncthreads();
     if (!s_last) return;
     __threadfence();                           // see every other chunk's totals
 
     // The sequence's last workgroup: outputs that depend on n only ...
-    if (threadIdx.x < g1) {
+    if (FUSED && threadIdx.x < g1) {
         const int i = threadIdx.x;
         row_max[(size_t)b * g1 + i] = r_m[i];
         row_sum[(size_t)b * g1 + i] = r_s[i];
@@ -357,7 +408,36 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
     }
 }
 
+// The draw for one sequence from the chunk totals draw_kernel<false> wrote.
+__global__ __launch_bounds__(kBlock) void pick_kernel(
+    const float* __restrict__ logits, const float* __restrict__ q,
+    const float* __restrict__ uniforms, int gamma, int V, int NC, const double* __restrict__ csum,
+    const double* __restrict__ psum, const float* __restrict__ row_max,
+    const float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
+    const int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
+    const int b = blockIdx.x;
+    const int g1 = gamma + 1;
+    const int n = n_accepted[b];
+    const size_t k = (size_t)b * g1 + n;
+    DrawRow d;
+    d.lrow = logits + k * V;
+    d.qrow = n < gamma ? q + ((size_t)b * gamma + n) * V : nullptr;
+    d.M = row_max[k];
+    d.S = row_sum[k];
+    d.V = V;
+    int flags;
+    const int tok = pick(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], &flags);
+    if (threadIdx.x == 0) {
+        out_tokens[k] = tok;
+        if (flags) status[b] |= flags;
+    }
+}
+
 }  // namespace
+
+#ifndef SV_FUSE_MAX_GROUPS
+#define SV_FUSE_MAX_GROUPS 64
+#endif
 
 hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
                               int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
@@ -365,9 +445,30 @@ hipError_t launch_accept_draw(const float* logits, const float* part_max, const 
                               double* psum, int32_t* counters, float* row_max, float* row_sum,
                               int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
                               hipStream_t stream) {
-    draw_kernel<<<dim3((unsigned)NC * (unsigned)B), dim3(kBlock), 0, stream>>>(
-        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum, counters,
-        row_max, row_sum, out_tokens, n_accepted, status);
+    const unsigned groups = (unsigned)NC * (unsigned)B;
+    // Few draw workgroups: fuse the accept tests into each and let the last
+    // one pick (one launch).  Many: accept once per sequence, chunk totals,
+    // then the pick -- three launches, no workgroup repeats the accept tests
+    // and none waits on a device-wide fence.
+    if (groups <= SV_FUSE_MAX_GROUPS) {
+        draw_kernel<true><<<dim3(groups), dim3(kBlock), 0, stream>>>(
+            logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum,
+            counters, row_max, row_sum, out_tokens, n_accepted, status);
+        return hipGetLastError();
+    }
+    accept_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(logits, part_max, part_sum, NP, NPs, draft, q,
+                                                       uniforms, gamma, V, row_max, row_sum,
+                                                       out_tokens, n_accepted, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    draw_kernel<false><<<dim3(groups), dim3(kBlock), 0, stream>>>(
+        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum,
+        counters, row_max, row_sum, out_tokens, n_accepted, status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    pick_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(logits, q, uniforms, gamma, V, NC, csum, psum,
+                                                     row_max, row_sum, out_tokens, n_accepted,
+                                                     status);
     return hipGetLastError();
 }
 

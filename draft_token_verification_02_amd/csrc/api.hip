@@ -6,6 +6,9 @@
 
 namespace sv {
 int lmhead_grid(int V);
+hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
+                               float* logits, float* part_max, float* part_sum, int NPs,
+                               int32_t* counters, int n_counters, hipStream_t stream);
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
                          float* logits, float* part_max, float* part_sum, int NPs, int grid,
                          int32_t* counters, int n_counters, hipStream_t stream);
@@ -30,6 +33,11 @@ bool dims_ok(sv_dims d) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Softmax partials per row that stage 1 wrote for these dims.
+int lmhead_partials(int R, int V) {
+    return sv::lmhead_use_tiled(R, V) ? sv::lmhead_tiled_partials(V) : sv::lmhead_grid(V);
+}
+
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
@@ -42,9 +50,15 @@ sv_status check_workspace(const void* ws, size_t bytes, sv_dims dims) {
 
 sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* ws, hipStream_t s) {
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
-    hipError_t e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
-                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NPs,
-                                     sv::lmhead_grid(dims.V), at<int32_t>(ws, L.counters), dims.B, s);
+    hipError_t e;
+    if (sv::lmhead_use_tiled(L.R, dims.V))
+        e = sv::launch_lmhead_tiled(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
+                                    at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NPs,
+                                    at<int32_t>(ws, L.counters), dims.B, s);
+    else
+        e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
+                              at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NPs,
+                              sv::lmhead_grid(dims.V), at<int32_t>(ws, L.counters), dims.B, s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
@@ -53,7 +67,7 @@ sv_status stage2(const int32_t* draft, const float* q, const float* uniforms, sv
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     hipError_t e = sv::launch_accept_draw(
         at<float>(ws, L.logits), at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
-        sv::lmhead_grid(dims.V), L.NPs, dims.B, dims.gamma, dims.V, draft, q, uniforms, L.NC,
+        lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.gamma, dims.V, draft, q, uniforms, L.NC,
         at<double>(ws, L.csum), at<double>(ws, L.psum), at<int32_t>(ws, L.counters),
         at<float>(ws, L.row_max), at<float>(ws, L.row_sum), out_tokens, n_accepted,
         at<int32_t>(ws, L.status), s);

@@ -320,12 +320,20 @@ void launch_mt(dim3 g, dim3 b, hipStream_t s, const uint16_t* hidden, const uint
 // Workgroups of the LM-head launch (also the number of softmax partials per
 // row): one per compute unit, capped so every wave has fragments to stream.
 int lmhead_grid(int V) {
+    const int ntiles = (V + kLmTile - 1) / kLmTile;
     if (SV_LM_TILES_PER_WAVE > 0) {
-        const int ntiles = (V + kLmTile - 1) / kLmTile;
         const int per_wg = SV_LM_TILES_PER_WAVE * kLmWaves;
         return max(1, min((ntiles + per_wg - 1) / per_wg, lmhead_useful_groups(V)));
     }
-    return max(1, min(cu_count() * SV_LM_WG_PER_CU, lmhead_useful_groups(V)));
+    // One workgroup per CU at most, and just enough of them that every wave
+    // gets the same number of fragment groups (measured on the grouping of
+    // the one-hidden-fragment configuration, which all row counts share).
+    const int T1 = LmCfg<1>::T;
+    const int ngroups = (ntiles + T1 - 1) / T1;
+    const int waves = cu_count() * SV_LM_WG_PER_CU * kLmWaves;
+    const int per_wave = (ngroups + waves - 1) / waves;
+    const int grid = (ngroups + per_wave * kLmWaves - 1) / (per_wave * kLmWaves);
+    return max(1, min(grid, lmhead_useful_groups(V)));
 }
 
 // Enqueue the LM-head stage: one launch per group of up to 64 hidden rows.

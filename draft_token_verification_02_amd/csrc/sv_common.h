@@ -35,6 +35,14 @@ static inline int lmhead_useful_groups(int V) {
     return g < kLmMaxPartials ? g : kLmMaxPartials;
 }
 
+// Many-row LM-head path (an LDS-tiled MFMA GEMM, 256 x 256 blocks): used for
+// R > 64 as long as its per-block softmax partials fit the bound.
+constexpr int kLmTiledVocab = 256;
+static inline int lmhead_tiled_partials(int V) { return (V + kLmTiledVocab - 1) / kLmTiledVocab; }
+static inline bool lmhead_use_tiled(int R, int V) {
+    return R > kLmRowsPerPass && lmhead_tiled_partials(V) <= kLmMaxPartials;
+}
+
 // Byte offsets of every array inside the caller's workspace.  The partial
 // arrays have a row stride NPs (a multiple of 4, for 16-byte loads) that
 // bounds the LM-head grid on any device.
@@ -49,7 +57,10 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     (void)d;
     Layout L;
     L.R = B * (gamma + 1);
-    L.NPs = (lmhead_useful_groups(V) + 3) / 4 * 4;
+    const int np_tiled = lmhead_tiled_partials(V);
+    const int np = lmhead_use_tiled(L.R, V) && np_tiled > lmhead_useful_groups(V)
+                       ? np_tiled : lmhead_useful_groups(V);
+    L.NPs = (np + 3) / 4 * 4;
     L.NC = (V + kDrawChunk - 1) / kDrawChunk;
     size_t off = 0;
     L.logits = off;   off = align_up(off + (size_t)L.R * V * sizeof(float), 256);

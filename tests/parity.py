@@ -24,14 +24,15 @@ P_ATOL = 1e-5
 
 
 def to_device(x: dict, dev):
+    """Upload through pinned host copies (one copy engine transfer each)."""
     import torch
     t = {}
     for k, v in x.items():
         a = np.ascontiguousarray(v)
         if a.dtype == np.uint16:
-            t[k] = torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            t[k] = torch.from_numpy(a.view(np.int16)).pin_memory().to(dev).view(torch.bfloat16)
         else:
-            t[k] = torch.from_numpy(a).to(dev)
+            t[k] = torch.from_numpy(a).pin_memory().to(dev)
     return t
 
 
