@@ -76,6 +76,14 @@ template <> struct LmCfg<3> { static constexpr int T = SV_LM3_T, U = SV_LM3_U; }
 template <> struct LmCfg<4> { static constexpr int T = SV_LM4_T, U = SV_LM4_U; };
 constexpr int kGenericU = 4;         // ring depth of the path for ragged d
 
+// Groups of T fragments a wave stages in LDS before writing them out: a
+// 32 KB stage per wave, at least one group.
+template <int MT, int T>
+constexpr int kStageGroups = (32768 / (MT * kLmTile * T * kLmTile * 4)) > 0
+                                 ? (32768 / (MT * kLmTile * T * kLmTile * 4)) : 1;
+
+__device__ __forceinline__ bool vec_store_ok(int V) { return (V & 3) == 0; }
+
 template <int MT, int T, int U, bool FAST>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int row0, int rows,
@@ -161,28 +169,48 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     float run_m[MT], run_s[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) { run_m[m] = -INFINITY; run_s[m] = 0.f; }
-    const bool vec_store = (V & 3) == 0;
+
+    // Logits are staged per wave in LDS (kStageGroups groups of T fragments,
+    // rows padded by 16 bytes so the 16-byte writes of one fragment hit
+    // distinct banks) and written out as whole-row segments -- one 1 KB
+    // contiguous store per row and 256 vocab entries -- when the stage is
+    // full and at the end, instead of 64-byte pieces of 16 rows in the middle
+    // of the read stream.
+    constexpr int kSeg = kStageGroups<MT, T> * T * kLmTile;    // floats per staged row
+    constexpr int kSegPad = kSeg + 4;
+    __shared__ __attribute__((aligned(16))) float stage[kLmWaves][MT * kLmTile][kSegPad];
+    float (*st)[kSegPad] = stage[wave];
+    int stage_first = gb, staged = 0;
+    auto flush = [&]() {
+        const int vbase = stage_first * T * kLmTile;
+        const int nvals = staged * T * kLmTile;
+        for (int rr = 0; rr < rows && rr < MT * kLmTile; ++rr) {
+            float* lrow = logits + (size_t)(row0 + rr) * V;
+            for (int j = lane * 4; j < nvals; j += kWave * 4) {
+                const int v = vbase + j;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&st[rr][j]);
+                if (vec_store_ok(V) && v + 3 < V) {
+                    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(lrow + v));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (v + i < V) lrow[v + i] = x[i];
+                }
+            }
+        }
+        stage_first += staged;
+        staged = 0;
+    };
     // Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment.
     auto epilogue = [&](int g) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const int rr = m * kLmTile + r16;
-            const bool row_ok = rr < rows;
-            float* lrow = logits + (size_t)(row0 + (row_ok ? rr : 0)) * V;
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const int v = (g * T + t) * kLmTile + kg * 4;
-                if (row_ok) {
-                    if (vec_store) {
-                        if (v < V) *reinterpret_cast<float4*>(lrow + v) =
-                            make_float4(acc[t][m][0], acc[t][m][1], acc[t][m][2], acc[t][m][3]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (v + i < V) lrow[v + i] = acc[t][m][i];
-                    }
-                }
+                *reinterpret_cast<f32x4*>(&st[m * kLmTile + r16][(staged * T + t) * kLmTile + kg * 4]) =
+                    acc[t][m];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (v + i < V) mx = fmaxf(mx, acc[t][m][i]);
@@ -201,6 +229,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 run_s[m] = sm;
             }
         }
+        if (++staged == kStageGroups<MT, T>) flush();
     };
 
     // Fill the ring, then stream: MFMA on the oldest slot, refill it.
@@ -261,6 +290,8 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
             }
         }
     }
+
+    if (staged > 0) flush();
 
     // One partial per hidden row for the whole workgroup.
     __shared__ float s_max[kLmWaves][MT * kLmTile];
