@@ -79,3 +79,56 @@ def test_some_pin_catches(name, monkeypatch):
         except Exception:            # a crash under the mutant also counts as caught
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutant {name}"
+
+
+# --------------------------------------------------------------------------
+# Greedy verification oracle.
+# --------------------------------------------------------------------------
+from oracle import greedy_ref as G          # noqa: E402
+from tests import test_oracle_greedy_pins as GP   # noqa: E402
+
+
+def _last_max(L):
+    M = np.where(np.isnan(L), -np.inf, L)
+    flipped = np.argmax(M[..., ::-1], axis=-1)
+    arg = (M.shape[-1] - 1 - flipped).astype(np.int64)
+    arg[~(M.max(axis=-1) > -np.inf)] = -1
+    return arg
+
+
+_ORIG_GT = G.greedy_tokens
+
+GREEDY_MUTANTS = {
+    # ties resolved to the highest id
+    "argmax_last": ("greedy_tokens", _last_max),
+    # each row judged by the next row's greedy token
+    "argmax_next_row": ("greedy_tokens", lambda L: np.roll(_ORIG_GT(L), -1)),
+    # argmin instead of argmax
+    "argmin": ("greedy_tokens", lambda L: np.argmin(np.where(np.isnan(L), np.inf, L), axis=-1)),
+    # a count of all matches instead of the leading ones
+    "count_not_prefix": ("first_rejection", lambda flags: int(sum(bool(f) for f in flags))),
+    # transposed GEMM operand order
+    "gemm_wrong_rows": ("lmhead_logits",
+                        lambda h, W, chunk_rows=8192: R.bf16_to_f64(h) @ R.bf16_to_f64(W)[::-1].T),
+}
+GREEDY_PINS = [
+    (GP.test_greedy_token_hand_cases, ()),
+    (GP.test_emitted_tokens_are_the_targets_own_all_drafts, ()),
+    (GP.test_low_temperature_sampling_rule_is_greedy, ()),
+    (GP.test_exact_tie_goes_to_lowest_id, ()),
+    (GP.test_random_config_invariants, ()),
+]
+
+
+@pytest.mark.parametrize("name", sorted(GREEDY_MUTANTS))
+def test_some_greedy_pin_catches(name, monkeypatch):
+    attr, fn = GREEDY_MUTANTS[name]
+    monkeypatch.setattr(G, attr, fn)
+    caught = []
+    for pin, args in GREEDY_PINS:
+        try:
+            if _fails(pin, *args):
+                caught.append(pin.__name__)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
