@@ -4,8 +4,8 @@ The compute lives in ``libspecverify.so`` (hand-written HIP kernels behind a C
 ABI, include/specverify.h); this package is its ctypes binding.
 """
 
-from ._lib import (Dims, SVError, accept_and_draw, debug_views, dims_of, library, lmhead,
-                   new_workspace, verify, workspace_bytes)
+from ._lib import (Dims, SVError, accept_and_draw, accept_greedy, debug_views, dims_of, library,
+                   lmhead, new_workspace, verify, verify_greedy, workspace_bytes)
 
-__all__ = ["Dims", "SVError", "accept_and_draw", "debug_views", "dims_of", "library", "lmhead",
-           "new_workspace", "verify", "workspace_bytes"]
+__all__ = ["Dims", "SVError", "accept_and_draw", "accept_greedy", "debug_views", "dims_of",
+           "library", "lmhead", "new_workspace", "verify", "verify_greedy", "workspace_bytes"]

@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_DIMS, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_DEVICE = range(6)
 SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE = 1, 2, 4
+ABI_VERSION = 2
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
-           "sv_accept_and_draw", "sv_debug_views")
+           "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views")
 
 
 class Dims(ctypes.Structure):
@@ -54,10 +55,14 @@ def _load():
         lib.sv_lmhead.argtypes = [vp, vp, Dims, vp, sz, vp]
         lib.sv_accept_and_draw.restype = st
         lib.sv_accept_and_draw.argtypes = [vp, vp, vp, Dims, vp, vp, vp, sz, vp]
+        lib.spec_verify_greedy.restype = st
+        lib.spec_verify_greedy.argtypes = [vp, vp, vp, Dims, vp, vp, vp, vp, sz, vp]
+        lib.sv_accept_greedy.restype = st
+        lib.sv_accept_greedy.argtypes = [vp, Dims, vp, vp, vp, vp, sz, vp]
         lib.sv_debug_views.restype = st
         lib.sv_debug_views.argtypes = [vp, Dims, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), ctypes.POINTER(vp)]
-        if lib.sv_abi_version() != 1:
+        if lib.sv_abi_version() != ABI_VERSION:
             raise ImportError(f"{LIB_PATH}: unexpected ABI version {lib.sv_abi_version()}")
         _LIB = lib
     return _LIB
@@ -147,6 +152,44 @@ def verify(hidden, W, draft, q, uniforms, *, out_tokens=None, n_accepted=None, w
     if st != SV_OK:
         raise SVError(st, "spec_verify")
     return out_tokens, n_accepted
+
+
+def verify_greedy(hidden, W, draft, *, out_tokens=None, n_accepted=None, target_tokens=None,
+                  workspace=None, stream=None):
+    """Greedy (match) verification; returns (out_tokens, n_accepted, target_tokens).
+
+    hidden bf16 [B, gamma+1, d]; W bf16 [V, d]; draft int32 [B, gamma].
+    target_tokens int32 [B, gamma+1] receives every row's greedy token.
+    """
+    import torch
+    _check_inputs(hidden, W, draft)
+    dims = dims_of(hidden, W)
+    dev = W.device
+    if out_tokens is None:
+        out_tokens = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((dims.B,), dtype=torch.int32, device=dev)
+    if target_tokens is None:
+        target_tokens = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(dims, dev)
+    st = _load().spec_verify_greedy(_ptr(hidden), _ptr(W), _ptr(draft), dims, _ptr(out_tokens),
+                                    _ptr(n_accepted), _ptr(target_tokens), _ptr(workspace),
+                                    workspace.numel(), _stream_handle(dev, stream))
+    if st != SV_OK:
+        raise SVError(st, "spec_verify_greedy")
+    return out_tokens, n_accepted, target_tokens
+
+
+def accept_greedy(dims: Dims, draft, out_tokens, n_accepted, workspace, *, target_tokens=None,
+                  stream=None):
+    """Greedy stage 2 from the partials stage 1 left in ``workspace``."""
+    tp = _ptr(target_tokens) if target_tokens is not None else ctypes.c_void_p(None)
+    st = _load().sv_accept_greedy(_ptr(draft), dims, _ptr(out_tokens), _ptr(n_accepted), tp,
+                                  _ptr(workspace), workspace.numel(),
+                                  _stream_handle(draft.device, stream))
+    if st != SV_OK:
+        raise SVError(st, "sv_accept_greedy")
 
 
 def lmhead(hidden, W, workspace, *, stream=None):

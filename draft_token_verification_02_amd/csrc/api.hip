@@ -7,11 +7,15 @@
 namespace sv {
 int lmhead_grid(int V);
 hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                               float* logits, float* part_max, float* part_sum, int NPs,
-                               int32_t* counters, int n_counters, hipStream_t stream);
+                               float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+                               int NPs, int32_t* counters, int n_counters, hipStream_t stream);
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                         float* logits, float* part_max, float* part_sum, int NPs, int grid,
-                         int32_t* counters, int n_counters, hipStream_t stream);
+                         float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+                         int NPs, int grid, int32_t* counters, int n_counters, hipStream_t stream);
+hipError_t launch_greedy(const float* part_max, const int32_t* part_arg, int NP, int NPs, int B,
+                         int gamma, int V, const int32_t* draft, int32_t* out_tokens,
+                         int32_t* n_accepted, int32_t* target_tokens, int32_t* status,
+                         hipStream_t stream);
 hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
                               int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
                               const float* q, const float* uniforms, int NC, double* csum,
@@ -48,17 +52,32 @@ sv_status check_workspace(const void* ws, size_t bytes, sv_dims dims) {
     return SV_OK;
 }
 
-sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* ws, hipStream_t s) {
+// keep_logits = false (greedy verification) writes only the partials.
+sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* ws, hipStream_t s,
+                 bool keep_logits = true) {
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
+    float* logits = keep_logits ? at<float>(ws, L.logits) : nullptr;
     hipError_t e;
     if (sv::lmhead_use_tiled(L.R, dims.V))
-        e = sv::launch_lmhead_tiled(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
-                                    at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NPs,
+        e = sv::launch_lmhead_tiled(hidden, W, L.R, dims.d, dims.V, logits,
+                                    at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
+                                    at<int32_t>(ws, L.part_arg), L.NPs,
                                     at<int32_t>(ws, L.counters), dims.B, s);
     else
-        e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, at<float>(ws, L.logits),
-                              at<float>(ws, L.part_max), at<float>(ws, L.part_sum), L.NPs,
-                              sv::lmhead_grid(dims.V), at<int32_t>(ws, L.counters), dims.B, s);
+        e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, logits,
+                              at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
+                              at<int32_t>(ws, L.part_arg), L.NPs, sv::lmhead_grid(dims.V),
+                              at<int32_t>(ws, L.counters), dims.B, s);
+    return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
+}
+
+sv_status stage2_greedy(const int32_t* draft, sv_dims dims, int32_t* out_tokens,
+                        int32_t* n_accepted, int32_t* target_tokens, void* ws, hipStream_t s) {
+    const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
+    hipError_t e = sv::launch_greedy(at<float>(ws, L.part_max), at<int32_t>(ws, L.part_arg),
+                                     lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.gamma,
+                                     dims.V, draft, out_tokens, n_accepted, target_tokens,
+                                     at<int32_t>(ws, L.status), s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
@@ -89,6 +108,17 @@ sv_status check_stage2(const int32_t* draft, const float* q, const float* unifor
     if (!draft || !q || !uniforms || !out_tokens || !n_accepted) return SV_ERR_NULL;
     if (!aligned(q, 16) || !aligned(draft, 4) || !aligned(uniforms, 4) || !aligned(out_tokens, 4) ||
         !aligned(n_accepted, 4))
+        return SV_ERR_ALIGN;
+    return check_workspace(ws, bytes, dims);
+}
+
+sv_status check_greedy(const int32_t* draft, sv_dims dims, const int32_t* out_tokens,
+                       const int32_t* n_accepted, const int32_t* target_tokens, const void* ws,
+                       size_t bytes) {
+    if (!dims_ok(dims)) return SV_ERR_DIMS;
+    if (!draft || !out_tokens || !n_accepted) return SV_ERR_NULL;
+    if (!aligned(draft, 4) || !aligned(out_tokens, 4) || !aligned(n_accepted, 4) ||
+        !aligned(target_tokens, 4))
         return SV_ERR_ALIGN;
     return check_workspace(ws, bytes, dims);
 }
@@ -144,6 +174,31 @@ sv_status spec_verify(const uint16_t* hidden, const uint16_t* W_lmhead, const in
     st = stage1(hidden, W_lmhead, dims, workspace, s);
     if (st != SV_OK) return st;
     return stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace, s);
+}
+
+sv_status sv_accept_greedy(const int32_t* draft_tokens, sv_dims dims, int32_t* out_tokens,
+                           int32_t* n_accepted, int32_t* target_tokens, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+    const sv_status st = check_greedy(draft_tokens, dims, out_tokens, n_accepted, target_tokens,
+                                      workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    return stage2_greedy(draft_tokens, dims, out_tokens, n_accepted, target_tokens, workspace,
+                         static_cast<hipStream_t>(hip_stream));
+}
+
+sv_status spec_verify_greedy(const uint16_t* hidden, const uint16_t* W_lmhead,
+                             const int32_t* draft_tokens, sv_dims dims, int32_t* out_tokens,
+                             int32_t* n_accepted, int32_t* target_tokens, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+    sv_status st = check_stage1(hidden, W_lmhead, dims, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    st = check_greedy(draft_tokens, dims, out_tokens, n_accepted, target_tokens, workspace,
+                      workspace_bytes);
+    if (st != SV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = stage1(hidden, W_lmhead, dims, workspace, s, /*keep_logits=*/false);
+    if (st != SV_OK) return st;
+    return stage2_greedy(draft_tokens, dims, out_tokens, n_accepted, target_tokens, workspace, s);
 }
 
 sv_status sv_debug_views(const void* workspace, sv_dims dims, const float** logits,

@@ -1,5 +1,6 @@
 // LM-head GEMM of the verification step: logits = hidden . W^T for all
-// B*(gamma+1) rows in one pass over W, plus per-workgroup softmax partials.
+// B*(gamma+1) rows in one pass over W, plus per-workgroup softmax and argmax
+// partials.
 //
 // Source: "推测解码" (world.lapla.si/zh/specdec), section 先让小模型猜 -- the
 // target scores every drafted position plus one in a single read of its
@@ -24,7 +25,9 @@
 // (max, sum exp) per row) overlaps the next group's loads.  Few rows per
 // wave with a deep ring keeps each wave's HBM accesses on few DRAM pages.
 // The workgroup reduces its running maxima and sums to one softmax partial
-// per row, so no later pass has to re-read the logits to normalise them.
+// per row, so no later pass has to re-read the logits to normalise them, and
+// its greedy candidates to one (largest logit, lowest id) pair per row, from
+// which greedy verification takes each row's argmax without the logits.
 
 #include "sv_common.h"
 
@@ -35,6 +38,11 @@
 // workgroup per CU, the vocabulary split over them).
 #ifndef SV_LM_TILES_PER_WAVE
 #define SV_LM_TILES_PER_WAVE 0
+#endif
+// Start each fragment group's walk over k at a hashed offset (see the
+// streaming loop); 0 walks every group from k = 0.
+#ifndef SV_LM_ROTATE
+#define SV_LM_ROTATE 1
 #endif
 
 namespace sv {
@@ -88,7 +96,8 @@ template <int MT, int T, int U, bool FAST>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int row0, int rows,
     int d, int V, float* __restrict__ logits, float* __restrict__ part_max,
-    float* __restrict__ part_sum, int NPs, int32_t* __restrict__ counters, int n_counters) {
+    float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
+    int32_t* __restrict__ counters, int n_counters) {
     const int lane = threadIdx.x & (kWave - 1);
     // The wave index is the same on every lane; saying so keeps the wave's
     // range, cursors and branches in scalar registers, which lets the
@@ -165,10 +174,15 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                     acc[t][m], 0, 0, 0);
     };
 
-    // Running softmax partial of this lane's hidden rows over its vocab entries.
-    float run_m[MT], run_s[MT];
+    // Running softmax partial of this lane's hidden rows over its vocab
+    // entries, and the running greedy candidate (largest logit, first id).
+    float run_m[MT], run_s[MT], run_av[MT];
+    int run_ai[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) { run_m[m] = -INFINITY; run_s[m] = 0.f; }
+    for (int m = 0; m < MT; ++m) { run_m[m] = -INFINITY; run_s[m] = 0.f; run_av[m] = -INFINITY; run_ai[m] = -1; }
+    // Without a logits buffer (greedy verification needs only the partials)
+    // nothing is staged or stored.
+    const bool keep_logits = logits != nullptr;
 
     // Logits are staged per wave in LDS (kStageGroups groups of T fragments,
     // rows padded by 16 bytes so the 16-byte writes of one fragment hit
@@ -201,7 +215,8 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         stage_first += staged;
         staged = 0;
     };
-    // Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment.
+    // Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment; its ids
+    // rise with t and i, and with g, so a strict '>' keeps the first maximum.
     auto epilogue = [&](int g) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -209,11 +224,15 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const int v = (g * T + t) * kLmTile + kg * 4;
-                *reinterpret_cast<f32x4*>(&st[m * kLmTile + r16][(staged * T + t) * kLmTile + kg * 4]) =
-                    acc[t][m];
+                if (keep_logits)
+                    *reinterpret_cast<f32x4*>(&st[m * kLmTile + r16][(staged * T + t) * kLmTile + kg * 4]) =
+                        acc[t][m];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (v + i < V) mx = fmaxf(mx, acc[t][m][i]);
+                    if (v + i < V) {
+                        mx = fmaxf(mx, acc[t][m][i]);
+                        if (acc[t][m][i] > run_av[m]) { run_av[m] = acc[t][m][i]; run_ai[m] = v + i; }
+                    }
             }
             if (mx != -INFINITY) {
                 const float nm = fmaxf(run_m[m], mx);
@@ -229,7 +248,10 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 run_s[m] = sm;
             }
         }
-        if (++staged == kStageGroups<MT, T>) flush();
+        if (++staged == kStageGroups<MT, T>) {
+            if (keep_logits) flush();
+            else { stage_first += staged; staged = 0; }
+        }
     };
 
     // Fill the ring, then stream: MFMA on the oldest slot, refill it.
@@ -252,9 +274,30 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                     for (int m = 0; m < MT; ++m) hr[u][m] = hp[m][(lk + u) * 4];
                 }
             };
+            // Each group walks its k-steps from a block of its own (a hash
+            // of the group index) and wraps; k is a pure reduction, so only
+            // the fp32 summation order changes.  Otherwise every wave reads
+            // the same offset within its rows at the same moment, and with a
+            // power-of-two row pitch (d = 4096: 8 KB) all requests in flight
+            // share their low address bits; the achieved bandwidth then
+            // depended on where the allocation of W happened to sit in HBM
+            // (175-217 us for the same 1 GB on four allocations, 179-181 us
+            // with the offsets spread).
+            const int nblk = nstep / U;
+            auto rot = [&](int g) {
+                return SV_LM_ROTATE ? (int)(((unsigned)g * 2654435761u >> 16) % (unsigned)nblk) * U : 0;
+            };
+            int lcnt = 0;                 // k-steps loaded in the current load group
+            lk = rot(lg);
             auto next_block = [&]() {
                 lk += U;
-                if (lk == nstep) { lk = 0; ++lg; if (lg < ge) set_rows(lg); }
+                lcnt += U;
+                if (lk == nstep) lk = 0;
+                if (lcnt == nstep) {
+                    lcnt = 0;
+                    ++lg;
+                    if (lg < ge) { set_rows(lg); lk = rot(lg); }
+                }
             };
             load_block();
             next_block();
@@ -291,32 +334,45 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         }
     }
 
-    if (staged > 0) flush();
+    if (keep_logits && staged > 0) flush();
 
     // One partial per hidden row for the whole workgroup.
     __shared__ float s_max[kLmWaves][MT * kLmTile];
     __shared__ float s_sum[kLmWaves][MT * kLmTile];
+    __shared__ float s_av[kLmWaves][MT * kLmTile];
+    __shared__ int s_ai[kLmWaves][MT * kLmTile];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        float mm = run_m[m], ss = run_s[m];
+        float mm = run_m[m], ss = run_s[m], av = run_av[m];
+        int ai = run_ai[m];
 #pragma unroll
         for (int off = 16; off < kWave; off <<= 1) {
             const float m2 = __shfl_xor(mm, off), s2 = __shfl_xor(ss, off);
             lse_merge(mm, ss, m2, s2);
+            const float av2 = __shfl_xor(av, off);
+            const int ai2 = __shfl_xor(ai, off);
+            arg_merge(av, ai, av2, ai2);
         }
         if (kg == 0) {
             s_max[wave][m * kLmTile + r16] = mm;
             s_sum[wave][m * kLmTile + r16] = ss;
+            s_av[wave][m * kLmTile + r16] = av;
+            s_ai[wave][m * kLmTile + r16] = ai;
         }
     }
     __syncthreads();
     if (threadIdx.x < MT * kLmTile && (int)threadIdx.x < rows) {
         const int rr = threadIdx.x;
-        float m = -INFINITY, s = 0.f;
+        float m = -INFINITY, s = 0.f, av = -INFINITY;
+        int ai = -1;
 #pragma unroll
-        for (int w = 0; w < kLmWaves; ++w) lse_merge(m, s, s_max[w][rr], s_sum[w][rr]);
+        for (int w = 0; w < kLmWaves; ++w) {
+            lse_merge(m, s, s_max[w][rr], s_sum[w][rr]);
+            arg_merge(av, ai, s_av[w][rr], s_ai[w][rr]);
+        }
         part_max[(size_t)(row0 + rr) * NPs + blockIdx.x] = m;
         part_sum[(size_t)(row0 + rr) * NPs + blockIdx.x] = s;
+        part_arg[(size_t)(row0 + rr) * NPs + blockIdx.x] = ai;
     }
 }
 
@@ -336,14 +392,14 @@ int cu_count() {
 
 template <int MT>
 void launch_mt(dim3 g, dim3 b, hipStream_t s, const uint16_t* hidden, const uint16_t* W, int row0,
-               int rows, int d, int V, float* logits, float* pm, float* ps, int NPs,
+               int rows, int d, int V, float* logits, float* pm, float* ps, int32_t* pa, int NPs,
                int32_t* counters, int nc) {
     constexpr int T = LmCfg<MT>::T, U = LmCfg<MT>::U;
     const int nstep = (d + 31) / 32;
     if (d % 32 == 0 && nstep % U == 0)
-        lmhead_kernel<MT, T, U, true><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, NPs, counters, nc);
+        lmhead_kernel<MT, T, U, true><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc);
     else
-        lmhead_kernel<MT, T, kGenericU, false><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, NPs, counters, nc);
+        lmhead_kernel<MT, T, kGenericU, false><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc);
 }
 
 }  // namespace
@@ -368,19 +424,20 @@ int lmhead_grid(int V) {
 }
 
 // Enqueue the LM-head stage: one launch per group of up to 64 hidden rows.
+// logits may be null: then only the partials are written.
 hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                         float* logits, float* part_max, float* part_sum, int NPs, int grid,
-                         int32_t* counters, int n_counters, hipStream_t stream) {
+                         float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+                         int NPs, int grid, int32_t* counters, int n_counters, hipStream_t stream) {
     for (int row0 = 0; row0 < R; row0 += kLmRowsPerPass) {
         const int rows = min(kLmRowsPerPass, R - row0);
         const int mt = (rows + kLmTile - 1) / kLmTile;
         const int nc = row0 == 0 ? n_counters : 0;
         dim3 g(grid), b(kLmWaves * kWave);
         switch (mt) {
-            case 1: launch_mt<1>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
-            case 2: launch_mt<2>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
-            case 3: launch_mt<3>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
-            default: launch_mt<4>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, NPs, counters, nc); break;
+            case 1: launch_mt<1>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
+            case 2: launch_mt<2>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
+            case 3: launch_mt<3>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
+            default: launch_mt<4>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -1,5 +1,6 @@
 // LM-head GEMM for many rows: logits = hidden . W^T with R > 64, plus one
-// softmax partial per (row, 256-entry vocab block).
+// softmax partial and one greedy candidate (largest logit, lowest id) per
+// (row, 256-entry vocab block).
 //
 // Source: "推测解码" (world.lapla.si/zh/specdec), sections 先让小模型猜 and
 // 几段话一起写 -- one read of the target's weights serves every drafted
@@ -82,11 +83,14 @@ __device__ __forceinline__ void store_stage(const Stage& s, char* lw, char* lh) 
 __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
-    float* __restrict__ part_sum, int NPs, int32_t* __restrict__ counters, int n_counters) {
+    float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
+    int32_t* __restrict__ counters, int n_counters) {
     // LDS: two stages of (W tile, hidden tile), each 256 rows x 144 bytes.
     __shared__ __attribute__((aligned(16))) char lds[2][2][kTV * kRowBytes];
     __shared__ float s_max[kTV / kWaveV][kTR];
     __shared__ float s_sum[kTV / kWaveV][kTR];
+    __shared__ float s_av[kTV / kWaveV][kTR];
+    __shared__ int s_ai[kTV / kWaveV][kTR];
 
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
         counters[i] = 0;
@@ -142,19 +146,22 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
         __syncthreads();
     }
 
-    // Epilogue: lane holds D[vocab 4*kg + i][row r16] of each fragment.
+    // Epilogue: lane holds D[vocab 4*kg + i][row r16] of each fragment; its
+    // ids rise with a and i, so a strict '>' keeps the first maximum.  No
+    // logits buffer: only the partials are written.
     const bool vec_store = (V & 3) == 0;
 #pragma unroll
     for (int b = 0; b < kFR; ++b) {
         const int rl = wr * kWaveR + b * kLmTile + r16;     // row within the block
         const int r = r0 + rl;
         const bool row_ok = r < R;
-        float* lrow = logits + (size_t)(row_ok ? r : 0) * V;
-        float mx = -INFINITY;
+        float* lrow = logits ? logits + (size_t)(row_ok ? r : 0) * V : nullptr;
+        float mx = -INFINITY, av = -INFINITY;
+        int ai = -1;
 #pragma unroll
         for (int a = 0; a < kFV; ++a) {
             const int v = v0 + wv * kWaveV + a * kLmTile + kg * 4;
-            if (row_ok) {
+            if (row_ok && lrow) {
                 if (vec_store) {
                     if (v < V) *reinterpret_cast<float4*>(lrow + v) =
                         make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
@@ -166,10 +173,19 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (v + i < V) mx = fmaxf(mx, acc[a][b][i]);
+                if (v + i < V) {
+                    mx = fmaxf(mx, acc[a][b][i]);
+                    if (acc[a][b][i] > av) { av = acc[a][b][i]; ai = v + i; }
+                }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) {
+            const float av2 = __shfl_xor(av, off);
+            const int ai2 = __shfl_xor(ai, off);
+            arg_merge(av, ai, av2, ai2);
+        }
         float sm = 0.f;
         if (mx != -INFINITY) {
 #pragma unroll
@@ -182,30 +198,35 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
         }
         sm += __shfl_xor(sm, 16);
         sm += __shfl_xor(sm, 32);
-        if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; }
+        if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; s_av[wv][rl] = av; s_ai[wv][rl] = ai; }
     }
     __syncthreads();
     if (threadIdx.x < kTR && r0 + (int)threadIdx.x < R) {
         const int rl = threadIdx.x;
-        float m = -INFINITY, s = 0.f;
+        float m = -INFINITY, s = 0.f, av = -INFINITY;
+        int ai = -1;
 #pragma unroll
-        for (int w = 0; w < kTV / kWaveV; ++w) lse_merge(m, s, s_max[w][rl], s_sum[w][rl]);
+        for (int w = 0; w < kTV / kWaveV; ++w) {
+            lse_merge(m, s, s_max[w][rl], s_sum[w][rl]);
+            arg_merge(av, ai, s_av[w][rl], s_ai[w][rl]);
+        }
         part_max[(size_t)(r0 + rl) * NPs + vb] = m;
         part_sum[(size_t)(r0 + rl) * NPs + vb] = s;
+        part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
     }
 }
 
 }  // namespace
 
 hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                               float* logits, float* part_max, float* part_sum, int NPs,
-                               int32_t* counters, int n_counters, hipStream_t stream) {
+                               float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+                               int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
     const int nvb = lmhead_tiled_partials(V);
     const int nrb = (R + kTR - 1) / kTR;
     const int nblocks = nvb * nrb;
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
     lmhead_tiled_kernel<<<dim3(grid), dim3(kTThreads), 0, stream>>>(
-        hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, NPs, counters, n_counters);
+        hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ static inline bool lmhead_use_tiled(int R, int V) {
 // bounds the LM-head grid on any device.
 struct Layout {
     int R, NPs, NC;
-    size_t logits, part_max, part_sum, row_max, row_sum, status, counters, csum, psum, total;
+    size_t logits, part_max, part_sum, part_arg, row_max, row_sum, status, counters, csum, psum,
+        total;
 };
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -66,6 +67,7 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     L.logits = off;   off = align_up(off + (size_t)L.R * V * sizeof(float), 256);
     L.part_max = off; off = align_up(off + (size_t)L.R * L.NPs * sizeof(float), 256);
     L.part_sum = off; off = align_up(off + (size_t)L.R * L.NPs * sizeof(float), 256);
+    L.part_arg = off; off = align_up(off + (size_t)L.R * L.NPs * sizeof(int32_t), 256);
     L.row_max = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
     L.row_sum = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
     L.status = off;   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
@@ -83,6 +85,16 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
     if (m == -INFINITY) { m = m2; s = s2; return; }
     if (m2 > m) { s = s * expf(m - m2) + s2; m = m2; }
     else        { s = s + s2 * expf(m2 - m); }
+}
+
+// Merge of two (value, token id) candidates for a row's greedy token: the
+// larger value wins, equal values go to the lower id, id -1 (no candidate)
+// loses.  A total order on the candidates, so any merge order and any
+// butterfly give the same answer on every lane.  Values are never NaN here:
+// candidates are only taken by a strict '>' against -inf or a previous value.
+__device__ __forceinline__ void arg_merge(float& v, int& i, float v2, int i2) {
+    if (i2 < 0) return;
+    if (i < 0 || v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
 }  // namespace sv

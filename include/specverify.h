@@ -56,7 +56,7 @@ extern "C" {
 #define SV_API
 #endif
 
-#define SV_ABI_VERSION 1
+#define SV_ABI_VERSION 2
 #define SV_MAX_GAMMA 32
 
 typedef struct {
@@ -78,7 +78,8 @@ typedef enum {
 /* Per-sequence device status bits (int32, one word per sequence). */
 #define SV_DEV_BAD_DRAFT 1  /* a draft id outside [0, V) was seen (treated as rejected) */
 #define SV_DEV_FALLBACK 2   /* the residual summed to <= 0; the replacement was drawn from p */
-#define SV_DEV_NONFINITE 4  /* no finite positive weights at all; token 0 was emitted */
+#define SV_DEV_NONFINITE 4  /* no finite positive weights at all (greedy: no logit above
+                               -inf in the emitting row); token 0 was emitted */
 
 /* ABI version of the loaded library (SV_ABI_VERSION). */
 SV_API int32_t sv_abi_version(void);
@@ -88,7 +89,7 @@ SV_API const char *sv_status_string(sv_status status);
 
 /* Bytes of device workspace one call needs for `dims`; 0 if dims are invalid.
  * The workspace holds the fp32 logits [R][V], the per-row softmax
- * normalisers and the draw's partial sums.  Its contents need no
+ * normalisers and argmax candidates, and the draw's partial sums.  Its contents need no
  * initialisation and are overwritten by every call. */
 SV_API size_t sv_workspace_bytes(sv_dims dims);
 
@@ -106,7 +107,7 @@ SV_API sv_status spec_verify(const uint16_t *hidden, const uint16_t *W_lmhead,
                       void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Stage 1 alone: the LM-head GEMM for all R rows in one pass over W, writing
- * the fp32 logits and per-tile softmax partials into the workspace.
+ * the fp32 logits and per-tile softmax and argmax partials into the workspace.
  * (Steps 1-2 above.) */
 SV_API sv_status sv_lmhead(const uint16_t *hidden, const uint16_t *W_lmhead, sv_dims dims,
                     void *workspace, size_t workspace_bytes, void *hip_stream);
@@ -118,6 +119,33 @@ SV_API sv_status sv_lmhead(const uint16_t *hidden, const uint16_t *W_lmhead, sv_
 SV_API sv_status sv_accept_and_draw(const int32_t *draft_tokens, const float *q, const float *uniforms,
                              sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
                              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Greedy (match) verification -- the deterministic form of the same step.
+ * The target's prediction at row i is its greedy token t_i: the largest
+ * logit of the row, the lowest id among equal maxima (NaN never wins).
+ * Draft i is kept while draft[b][i] == t_i; at the first mismatch n (or n =
+ * gamma when all match) t_n is emitted, so out_tokens[b] = t_0..t_n, -1 after:
+ * exactly the target's own greedy continuation.  (The maxstudionews.com
+ * article 1664 on multi-token prediction for Gemini Nano, paragraphs on the
+ * draft / verify split and on bit-identical output; "推测解码", section
+ * 先让小模型猜: guess-then-check in its greedy form.)
+ *   hidden, W_lmhead, draft_tokens, out_tokens, n_accepted  as for spec_verify
+ *   target_tokens int32 [B][gamma+1] or NULL  t_i of every row (-1 where a row
+ *                 has no logit above -inf)
+ * No q and no uniforms.  The logits are not stored (only per-workgroup
+ * argmax and softmax partials): after this call the workspace's logits,
+ * row_max and row_sumexp views are stale; status is valid. */
+SV_API sv_status spec_verify_greedy(const uint16_t *hidden, const uint16_t *W_lmhead,
+                             const int32_t *draft_tokens, sv_dims dims, int32_t *out_tokens,
+                             int32_t *n_accepted, int32_t *target_tokens, void *workspace,
+                             size_t workspace_bytes, void *hip_stream);
+
+/* Stage 2 of greedy verification alone, after sv_lmhead (or a previous
+ * spec_verify_greedy) on the same workspace, dims and device.  Arguments as
+ * for spec_verify_greedy. */
+SV_API sv_status sv_accept_greedy(const int32_t *draft_tokens, sv_dims dims, int32_t *out_tokens,
+                           int32_t *n_accepted, int32_t *target_tokens, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
 
 /* Device pointers into `workspace` for inspection after a call completes:
  *   logits      fp32 [R][V]

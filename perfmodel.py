@@ -65,3 +65,11 @@ def step_bytes(B: int, gamma: int, d: int, V: int, n_rejected: int) -> int:
 
 def lmhead_flops(B: int, gamma: int, d: int, V: int) -> int:
     return 2 * rows(B, gamma) * V * d
+
+
+def greedy_step_bytes(B: int, gamma: int, d: int, V: int) -> int:
+    """Minimum HBM bytes of greedy verification: W and hidden read once; the
+    argmax needs no logits in memory.  Plus drafts and outputs."""
+    R = rows(B, gamma)
+    small = 4 * B * gamma + 4 * B * (gamma + 1) * 2 + 4 * B
+    return 2 * V * d + 2 * R * d + small

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for name in _declared():
         assert hasattr(raw, name), name
-    assert lib.sv_abi_version() == 1
+    assert lib.sv_abi_version() == _lib.ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -80,6 +80,8 @@ def test_invalid_dims(dims):
     assert lib.spec_verify(p, p, p, p, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     assert lib.sv_lmhead(p, p, d, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     assert lib.sv_accept_and_draw(p, p, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
+    assert lib.spec_verify_greedy(p, p, p, d, p, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
+    assert lib.sv_accept_greedy(p, d, p, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     out = ctypes.c_void_p()
     assert lib.sv_debug_views(p, d, ctypes.byref(out), None, None, None) == _lib.SV_ERR_DIMS
 
@@ -110,6 +112,32 @@ def test_argument_errors_return_before_launch():
     assert lib.sv_accept_and_draw(p, p, p, d, p, p, p, n - 1, None) == _lib.SV_ERR_WORKSPACE
     assert lib.sv_lmhead(z, p, d, p, n, None) == _lib.SV_ERR_NULL
     assert lib.sv_accept_and_draw(p, z, p, d, p, p, p, n, None) == _lib.SV_ERR_NULL
+
+
+@no_device
+def test_greedy_argument_errors_return_before_launch():
+    lib = _lib.library()
+    d = _lib.Dims(2, 3, 64, 1000)
+    n = _lib.workspace_bytes(d)
+    p = ctypes.c_void_p(FAKE)
+    z = ctypes.c_void_p(0)
+    odd = ctypes.c_void_p(FAKE + 2)
+    # hidden, W, draft, out, n_accepted, workspace NULL in turn (target_tokens may be NULL,
+    # but with every other pointer fake the call then fails on something else first)
+    for k in (0, 1, 2, 3, 4, 6):
+        args = [p] * 7
+        args[k] = z
+        assert lib.spec_verify_greedy(*args[:3], d, *args[3:7], n, None) == _lib.SV_ERR_NULL, k
+    assert lib.spec_verify_greedy(odd, p, p, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_greedy(p, odd, p, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_greedy(p, p, odd, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_greedy(p, p, p, d, p, p, odd, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_greedy(p, p, p, d, p, p, p, ctypes.c_void_p(FAKE + 16), n, None) == \
+        _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_greedy(p, p, p, d, p, p, p, p, n - 1, None) == _lib.SV_ERR_WORKSPACE
+    assert lib.sv_accept_greedy(z, d, p, p, None, p, n, None) == _lib.SV_ERR_NULL
+    assert lib.sv_accept_greedy(p, d, z, p, None, p, n, None) == _lib.SV_ERR_NULL
+    assert lib.sv_accept_greedy(p, d, p, p, None, p, n - 1, None) == _lib.SV_ERR_WORKSPACE
 
 
 def test_debug_views_is_pointer_arithmetic():
