@@ -132,3 +132,48 @@ def test_some_greedy_pin_catches(name, monkeypatch):
         except Exception:
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutant {name}"
+
+
+# --------------------------------------------------------------------------
+# Clustered sparse head oracle.
+# --------------------------------------------------------------------------
+from oracle import sparse_ref as S            # noqa: E402
+from tests import test_oracle_sparse_pins as SP   # noqa: E402
+
+_ORIG_SEL = S.selected_tokens
+
+SPARSE_MUTANTS = {
+    # the k smallest cluster logits
+    "topk_smallest": ("top_clusters", lambda s, k: np.sort(np.argsort(s, kind="stable")[:k])),
+    # ties to the higher index
+    "topk_ties_high": ("top_clusters",
+                       lambda s, k: np.sort(len(s) - 1 - np.argsort(-s[::-1], kind="stable")[:k])),
+    # members of the neighbouring clusters
+    "wrong_members": ("selected_tokens",
+                      lambda m, c: _ORIG_SEL(m, (c + 1) % m.shape[0])),
+    # centroid table transposed against the hidden rows (rows reversed)
+    "cluster_scores_reversed": ("cluster_logits",
+                                lambda h, c: R.bf16_to_f64(h) @ R.bf16_to_f64(c)[::-1].T),
+}
+
+SPARSE_PINS = [
+    (SP.test_top_clusters_hand_cases, ()),
+    (SP.test_top_clusters_brute_force, ()),
+    (SP.test_all_clusters_is_the_full_softmax, ()),
+    (SP.test_singleton_clusters_select_top_tokens, ()),
+    (SP.test_values_follow_exact_logit_ratios, ()),
+]
+
+
+@pytest.mark.parametrize("name", sorted(SPARSE_MUTANTS))
+def test_some_sparse_pin_catches(name, monkeypatch):
+    attr, fn = SPARSE_MUTANTS[name]
+    monkeypatch.setattr(S, attr, fn)
+    caught = []
+    for pin, args in SPARSE_PINS:
+        try:
+            if _fails(pin, *args):
+                caught.append(pin.__name__)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
