@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kRowThreads = 32;
 constexpr int kRowsPerPass = kBlock / kRowThreads;
+constexpr int kBatch = 2;                 // 16-byte loads per thread per batch and array
 
 __global__ __launch_bounds__(kBlock) void greedy_kernel(
     const float* __restrict__ part_max, const int32_t* __restrict__ part_arg, int NP, int NPs,
@@ -46,9 +47,31 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
         float v = -INFINITY;
         int a = -1;
         if (i < g1) {
+            // 16-byte loads (rows of NPs, a multiple of 4), a batch of
+            // kBatch per thread issued before any is merged: one memory
+            // round trip for up to 32 * 4 * kBatch partials.
             const size_t r = (size_t)b * g1 + i;
-            for (int j = sub; j < NP; j += kRowThreads)
-                arg_merge(v, a, part_max[r * NPs + j], part_arg[r * NPs + j]);
+            const float4* pm = reinterpret_cast<const float4*>(part_max + r * NPs);
+            const int4* pa = reinterpret_cast<const int4*>(part_arg + r * NPs);
+            const int n4 = (NP + 3) / 4;
+            for (int j0 = 0; j0 < n4; j0 += kBatch * kRowThreads) {
+                float4 mv[kBatch];
+                int4 av[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int jj = j0 + sub + u * kRowThreads;
+                    mv[u] = jj < n4 ? pm[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    av[u] = jj < n4 ? pa[jj] : make_int4(-1, -1, -1, -1);
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int j = 4 * (j0 + sub + u * kRowThreads);   // entries past NP are padding
+                    if (j + 0 < NP) arg_merge(v, a, mv[u].x, av[u].x);
+                    if (j + 1 < NP) arg_merge(v, a, mv[u].y, av[u].y);
+                    if (j + 2 < NP) arg_merge(v, a, mv[u].z, av[u].z);
+                    if (j + 3 < NP) arg_merge(v, a, mv[u].w, av[u].w);
+                }
+            }
         }
 #pragma unroll
         for (int off = 1; off < kRowThreads; off <<= 1) {
