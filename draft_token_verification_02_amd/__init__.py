@@ -4,8 +4,12 @@ The compute lives in ``libspecverify.so`` (hand-written HIP kernels behind a C
 ABI, include/specverify.h); this package is its ctypes binding.
 """
 
-from ._lib import (Dims, SVError, accept_and_draw, accept_greedy, debug_views, dims_of, library,
-                   lmhead, new_workspace, verify, verify_greedy, workspace_bytes)
+from ._lib import (Dims, HeadDims, SVError, accept_and_draw, accept_and_draw_sparse_q,
+                   accept_greedy, debug_views, dims_of, library, lmhead, new_workspace,
+                   sparse_head, sparse_head_workspace_bytes, verify, verify_greedy,
+                   verify_sparse_q, workspace_bytes)
 
-__all__ = ["Dims", "SVError", "accept_and_draw", "accept_greedy", "debug_views", "dims_of",
-           "library", "lmhead", "new_workspace", "verify", "verify_greedy", "workspace_bytes"]
+__all__ = ["Dims", "HeadDims", "SVError", "accept_and_draw", "accept_and_draw_sparse_q",
+           "accept_greedy", "debug_views", "dims_of", "library", "lmhead", "new_workspace",
+           "sparse_head", "sparse_head_workspace_bytes", "verify", "verify_greedy",
+           "verify_sparse_q", "workspace_bytes"]

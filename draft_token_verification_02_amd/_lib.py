@@ -16,15 +16,22 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_DIMS, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_DEVICE = range(6)
-SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE = 1, 2, 4
-ABI_VERSION = 2
+SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE, SV_DEV_BAD_QID = 1, 2, 4, 8
+ABI_VERSION = 3
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
-           "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views")
+           "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views",
+           "spec_verify_sparse_q", "sv_accept_and_draw_sparse_q", "sv_sparse_head_workspace_bytes",
+           "sv_sparse_head")
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("gamma", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("V", ctypes.c_int32)]
+
+
+class HeadDims(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("d", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("C", ctypes.c_int32), ("M", ctypes.c_int32), ("k", ctypes.c_int32)]
 
 
 class SVError(RuntimeError):
@@ -59,6 +66,16 @@ def _load():
         lib.spec_verify_greedy.argtypes = [vp, vp, vp, Dims, vp, vp, vp, vp, sz, vp]
         lib.sv_accept_greedy.restype = st
         lib.sv_accept_greedy.argtypes = [vp, Dims, vp, vp, vp, vp, sz, vp]
+        lib.spec_verify_sparse_q.restype = st
+        lib.spec_verify_sparse_q.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int32, vp, Dims, vp, vp,
+                                             vp, sz, vp]
+        lib.sv_accept_and_draw_sparse_q.restype = st
+        lib.sv_accept_and_draw_sparse_q.argtypes = [vp, vp, vp, ctypes.c_int32, vp, Dims, vp, vp,
+                                                    vp, sz, vp]
+        lib.sv_sparse_head_workspace_bytes.restype = sz
+        lib.sv_sparse_head_workspace_bytes.argtypes = [HeadDims]
+        lib.sv_sparse_head.restype = st
+        lib.sv_sparse_head.argtypes = [vp, vp, vp, vp, HeadDims, vp, vp, vp, vp, sz, vp]
         lib.sv_debug_views.restype = st
         lib.sv_debug_views.argtypes = [vp, Dims, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), ctypes.POINTER(vp)]
@@ -210,6 +227,100 @@ def accept_and_draw(dims: Dims, draft, q, uniforms, out_tokens, n_accepted, work
                                     _stream_handle(q.device, stream))
     if st != SV_OK:
         raise SVError(st, "sv_accept_and_draw")
+
+
+def _check_sparse_q(dims: Dims, q_ids, q_vals):
+    import torch
+    if q_ids.dtype != torch.int32 or q_vals.dtype != torch.float32:
+        raise TypeError("q_ids must be int32 and q_vals float32")
+    if q_ids.dim() != 3 or tuple(q_ids.shape[:2]) != (dims.B, dims.gamma):
+        raise ValueError(f"q_ids must be [{dims.B}, {dims.gamma}, K], got {tuple(q_ids.shape)}")
+    if q_vals.shape != q_ids.shape:
+        raise ValueError("q_vals must have the shape of q_ids")
+    if not (q_ids.is_contiguous() and q_vals.is_contiguous()):
+        raise ValueError("q_ids and q_vals must be contiguous")
+    return int(q_ids.shape[2])
+
+
+def verify_sparse_q(hidden, W, draft, q_ids, q_vals, uniforms, *, out_tokens=None,
+                    n_accepted=None, workspace=None, stream=None):
+    """Verification with sparse q; returns (out_tokens [B, gamma+1], n_accepted [B]).
+
+    q_ids int32 [B, gamma, K] (ids < 0 are padding), q_vals float32 [B, gamma, K]:
+    the same result as ``verify`` on the dense q holding those values at those ids.
+    """
+    import torch
+    _check_inputs(hidden, W, draft, None, uniforms)
+    dims = dims_of(hidden, W)
+    K = _check_sparse_q(dims, q_ids, q_vals)
+    dev = W.device
+    if out_tokens is None:
+        out_tokens = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((dims.B,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(dims, dev)
+    st = _load().spec_verify_sparse_q(_ptr(hidden), _ptr(W), _ptr(draft), _ptr(q_ids),
+                                      _ptr(q_vals), K, _ptr(uniforms), dims, _ptr(out_tokens),
+                                      _ptr(n_accepted), _ptr(workspace), workspace.numel(),
+                                      _stream_handle(dev, stream))
+    if st != SV_OK:
+        raise SVError(st, "spec_verify_sparse_q")
+    return out_tokens, n_accepted
+
+
+def accept_and_draw_sparse_q(dims: Dims, draft, q_ids, q_vals, uniforms, out_tokens, n_accepted,
+                             workspace, *, stream=None):
+    """Stage 2 with sparse q, from stage 1's workspace."""
+    K = _check_sparse_q(dims, q_ids, q_vals)
+    st = _load().sv_accept_and_draw_sparse_q(_ptr(draft), _ptr(q_ids), _ptr(q_vals), K,
+                                             _ptr(uniforms), dims, _ptr(out_tokens),
+                                             _ptr(n_accepted), _ptr(workspace), workspace.numel(),
+                                             _stream_handle(q_vals.device, stream))
+    if st != SV_OK:
+        raise SVError(st, "sv_accept_and_draw_sparse_q")
+
+
+def sparse_head_workspace_bytes(dims: HeadDims) -> int:
+    return int(_load().sv_sparse_head_workspace_bytes(dims))
+
+
+def sparse_head(h, W, centroids, members, k: int, *, q_ids=None, q_vals=None, clusters=None,
+                workspace=None, stream=None):
+    """The drafter's clustered sparse head; returns (q_ids [N, k*M], q_vals [N, k*M], clusters [N, k]).
+
+    h bf16 [N, d]; W bf16 [V, d]; centroids bf16 [C, d]; members int32 [C, M].
+    """
+    import torch
+    dev = W.device
+    for name, t, dt in (("h", h, (torch.bfloat16, torch.int16, torch.uint16)),
+                        ("W", W, (torch.bfloat16, torch.int16, torch.uint16)),
+                        ("centroids", centroids, (torch.bfloat16, torch.int16, torch.uint16)),
+                        ("members", members, (torch.int32,))):
+        if t.device != dev or t.dtype not in dt or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name}: expected a contiguous 2-d {dt} tensor on {dev}")
+    N, d = h.shape
+    C, M = members.shape
+    if W.shape[1] != d or tuple(centroids.shape) != (C, d):
+        raise ValueError("W must be [V, d] and centroids [C, d] with the hidden size of h")
+    dims = HeadDims(N, d, W.shape[0], C, M, k)
+    nbytes = sparse_head_workspace_bytes(dims)
+    if nbytes == 0:
+        raise SVError(SV_ERR_DIMS, "sv_sparse_head_workspace_bytes")
+    if q_ids is None:
+        q_ids = torch.empty((N, k * M), dtype=torch.int32, device=dev)
+    if q_vals is None:
+        q_vals = torch.empty((N, k * M), dtype=torch.float32, device=dev)
+    if clusters is None:
+        clusters = torch.empty((N, k), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    st = _load().sv_sparse_head(_ptr(h), _ptr(W), _ptr(centroids), _ptr(members), dims,
+                                _ptr(q_ids), _ptr(q_vals), _ptr(clusters), _ptr(workspace),
+                                workspace.numel(), _stream_handle(dev, stream))
+    if st != SV_OK:
+        raise SVError(st, "sv_sparse_head")
+    return q_ids, q_vals, clusters
 
 
 def debug_views(workspace, dims: Dims) -> dict:

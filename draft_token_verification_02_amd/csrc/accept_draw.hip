@@ -27,6 +27,14 @@
 // the chunk) and the step needs no extra kernel boundary.  With many,
 // accept_kernel runs them once per sequence first and the chunk workgroups
 // read n and the draw row's normaliser from memory.
+//
+// q comes in one of two forms.  Dense: a full [V] row per drafted position.
+// Sparse: K (id, value) entries per row -- the drafter's clustered head
+// ("多詞元預測視覺化指南", section 高效嵌入器) gives q only on the tokens of its
+// chosen clusters and exactly 0 elsewhere.  With sparse q a drafted token's
+// q is found by one wave scanning the row's ids, and a draw workgroup builds
+// its chunk of the dense row in LDS (zeroed, then the row's entries that fall
+// in the chunk scattered in), so the draw arithmetic is the same in both.
 
 #include "sv_common.h"
 
@@ -40,6 +48,57 @@ constexpr int kMergeLoads = 2;                   // float4 loads per thread per 
 
 __device__ __forceinline__ float target_prob(float logit, float row_max, float row_sum) {
     return expf(logit - row_max) / row_sum;
+}
+
+// The drafter's q at the gamma drafted positions of every sequence.
+//   dense:  val [B][gamma][V], idx == nullptr;
+//   sparse: idx / val [B][gamma][K]: ids in [0, V) listed once each, ids < 0
+//           are padding; a token not listed has q = 0.  Sparse values that
+//           are negative or NaN count as 0, and an id listed more than once
+//           takes the largest of its values (the same rule in the accept
+//           test and in the draw, so the result stays deterministic).
+struct QArg {
+    const float* val;
+    const int32_t* idx;
+    int K;
+};
+
+// A sparse value as it is used: negative, -0 and NaN become +0, so the bit
+// pattern orders like the value (the LDS chunk merges entries by unsigned max).
+__device__ __forceinline__ float sparse_value(float v) { return v > 0.f ? v : 0.f; }
+
+// q of token x in one sparse row, by a whole wave: every lane scans its share
+// of the K ids (16-byte loads when the row allows), then a wave max.  Also
+// reports whether the row lists an id >= V.
+__device__ float sparse_lookup(const int32_t* __restrict__ ids, const float* __restrict__ vals, int K,
+                               int x, int V, bool* bad_id) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float best = 0.f;
+    bool bad = false;
+    if ((K & 3) == 0) {
+        const int4* id4 = reinterpret_cast<const int4*>(ids);
+        const int K4 = K >> 2;
+#pragma unroll 4
+        for (int j = lane; j < K4; j += kWave) {
+            const int4 v = id4[j];
+            bad |= v.x >= V || v.y >= V || v.z >= V || v.w >= V;
+            if (v.x == x) best = fmaxf(best, sparse_value(vals[4 * j + 0]));
+            if (v.y == x) best = fmaxf(best, sparse_value(vals[4 * j + 1]));
+            if (v.z == x) best = fmaxf(best, sparse_value(vals[4 * j + 2]));
+            if (v.w == x) best = fmaxf(best, sparse_value(vals[4 * j + 3]));
+        }
+    } else {
+#pragma unroll 4
+        for (int j = lane; j < K; j += kWave) {
+            const int id = ids[j];
+            bad |= id >= V;
+            if (id == x) best = fmaxf(best, sparse_value(vals[j]));
+        }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    *bad_id = __ballot(bad) != 0;
+    return best;
 }
 
 // Inclusive prefix sum of one double per thread over the workgroup, in a
@@ -98,12 +157,16 @@ __device__ __forceinline__ int block_max_int(int v) { return -block_min_int(-v);
 
 // ---------------------------------------------------------------------------
 // Steps 1-2: softmax normalisers of the sequence's rows (into r_m, r_s) and
-// the accept tests.  Returns n; *bad is set when a draft id was out of range.
+// the accept tests.  Returns n; *flags gets SV_DEV_BAD_DRAFT when a draft id
+// was out of range and SV_DEV_BAD_QID when a sparse q row lists an id >= V.
+template <bool SPARSE>
 __device__ int accept_tests(const float* __restrict__ logits, const float* __restrict__ part_max,
                             const float* __restrict__ part_sum, int NP, int NPs, int b, int gamma,
-                            int V, const int32_t* __restrict__ draft, const float* __restrict__ q,
-                            const float* __restrict__ uniforms, float* r_m, float* r_s, bool* bad) {
-    __shared__ int s_n, s_bad;
+                            int V, const int32_t* __restrict__ draft, QArg q,
+                            const float* __restrict__ uniforms, float* r_m, float* r_s, int* flags) {
+    __shared__ int s_n, s_flags;
+    __shared__ float s_qx[SPARSE ? SV_MAX_GAMMA : 1];
+    __shared__ int s_badq[SPARSE ? kBlock / kWave : 1];
     const int g1 = gamma + 1;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -117,8 +180,21 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
         ux = uniforms[(size_t)b * g1 + lane];
         if (valid) {
             lx = logits[((size_t)b * g1 + lane) * V + x];
-            qx = q[((size_t)b * gamma + lane) * V + x];
+            if (!SPARSE) qx = q.val[((size_t)b * gamma + lane) * V + x];
         }
+    }
+    if (SPARSE) {
+        // One wave per drafted position looks its token up in the q row.
+        bool badq = false;
+        for (int i = wave; i < gamma; i += kBlock / kWave) {
+            const int x = draft[(size_t)b * gamma + i];
+            const size_t row = ((size_t)b * gamma + i) * (size_t)q.K;
+            bool bad_id;
+            const float v = sparse_lookup(q.idx + row, q.val + row, q.K, x, V, &bad_id);
+            badq |= bad_id;
+            if (lane == 0) s_qx[i] = v;
+        }
+        if (lane == 0) s_badq[wave] = badq;
     }
 
     // 32 threads per row, 8 rows per pass.  A batch is kMergeLoads float4 of
@@ -175,29 +251,90 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
     __syncthreads();
 
     if (wave == 0) {
+        if (SPARSE && lane < gamma) qx = s_qx[lane];
         bool keep = false;
         if (lane < gamma && valid) keep = ux * qx <= target_prob(lx, r_m[lane], r_s[lane]);
         const unsigned long long kept = __ballot(keep);
         const unsigned long long badm = __ballot(lane < gamma && !valid);
         if (lane == 0) {
             s_n = min(__builtin_ctzll(~kept), gamma);
-            s_bad = badm != 0;
+            int f = badm != 0 ? SV_DEV_BAD_DRAFT : 0;
+            if (SPARSE) {
+#pragma unroll
+                for (int w = 0; w < kBlock / kWave; ++w)
+                    if (s_badq[w]) f |= SV_DEV_BAD_QID;
+            }
+            s_flags = f;
         }
     }
     __syncthreads();
-    *bad = s_bad;
+    *flags = s_flags;
     return s_n;
 }
 
 // ---------------------------------------------------------------------------
 // The row a sequence draws from: its logits, the q of the rejected draft
-// (nullptr for the bonus draw), and its softmax normaliser.
+// (none for the bonus draw), and its softmax normaliser.
 struct DrawRow {
     const float* lrow;
-    const float* qrow;
+    const float* qrow;        // dense q row, or nullptr
+    const int32_t* qids;      // sparse q row, or nullptr
+    const float* qvals;
+    int K;
     float M, S;
     int V;
+    __device__ bool has_q() const { return qrow != nullptr || qids != nullptr; }
+    __device__ void drop_q() { qrow = nullptr; qids = nullptr; }
 };
+
+template <bool SPARSE>
+__device__ __forceinline__ DrawRow draw_row(const float* logits, QArg q, int b, int gamma, int n,
+                                            int V, float M, float S) {
+    DrawRow d;
+    const size_t k = (size_t)b * (gamma + 1) + n;
+    d.lrow = logits + k * V;
+    d.qrow = nullptr;
+    d.qids = nullptr;
+    d.qvals = nullptr;
+    d.K = q.K;
+    if (n < gamma) {
+        const size_t r = (size_t)b * gamma + n;
+        if (SPARSE) { d.qids = q.idx + r * q.K; d.qvals = q.val + r * q.K; }
+        else        { d.qrow = q.val + r * V; }
+    }
+    d.M = M;
+    d.S = S;
+    d.V = V;
+    return d;
+}
+
+// The dense q of chunk [c0, c0 + kDrawChunk) of a sparse row, built in LDS:
+// zeroed, then every entry whose id falls in the chunk merged in by unsigned
+// max on the value's bits (values were made non-negative, where the bit
+// order is the value order).  Every thread of the workgroup takes part.
+__device__ void stage_sparse_chunk(const DrawRow& d, int c0, unsigned* s_qc) {
+    for (int j = threadIdx.x; j < kDrawChunk; j += kBlock) s_qc[j] = 0u;
+    __syncthreads();
+    auto put = [&](int id, float v) {
+        const unsigned rel = (unsigned)(id - c0);
+        if (id >= 0 && id < d.V && rel < (unsigned)kDrawChunk)
+            atomicMax(&s_qc[rel], __float_as_uint(sparse_value(v)));
+    };
+    if ((d.K & 3) == 0) {
+        const int4* id4 = reinterpret_cast<const int4*>(d.qids);
+        const float4* v4 = reinterpret_cast<const float4*>(d.qvals);
+        const int K4 = d.K >> 2;
+#pragma unroll 4
+        for (int j = threadIdx.x; j < K4; j += kBlock) {
+            const int4 i = id4[j];
+            const float4 v = v4[j];
+            put(i.x, v.x); put(i.y, v.y); put(i.z, v.z); put(i.w, v.w);
+        }
+    } else {
+        for (int j = threadIdx.x; j < d.K; j += kBlock) put(d.qids[j], d.qvals[j]);
+    }
+    __syncthreads();
+}
 
 __device__ __forceinline__ void load16(const float* row, int j0, int V, float (&x)[kDrawPerThread]) {
     if (((V & 3) == 0) && j0 + kDrawPerThread <= V) {
@@ -216,24 +353,40 @@ __device__ __forceinline__ void load16(const float* row, int j0, int V, float (&
 }
 
 // Draw weights w and target probabilities p of 16 consecutive tokens from j0
-// (zero past the end of the vocabulary).
-__device__ __forceinline__ void draw_weights16(const DrawRow& d, int j0, float (&w)[kDrawPerThread],
-                                               float (&p)[kDrawPerThread]) {
+// (zero past the end of the vocabulary).  With sparse q, s_qc holds the
+// chunk starting at c0 (stage_sparse_chunk).
+template <bool SPARSE>
+__device__ __forceinline__ void draw_weights16(const DrawRow& d, int j0, const unsigned* s_qc, int c0,
+                                               float (&w)[kDrawPerThread], float (&p)[kDrawPerThread]) {
     float l[kDrawPerThread], qv[kDrawPerThread];
     load16(d.lrow, j0, d.V, l);
-    if (d.qrow) load16(d.qrow, j0, d.V, qv);
+    const bool has_q = d.has_q();
+    if (SPARSE) {
+        if (has_q) {
+            const uint4* src = reinterpret_cast<const uint4*>(s_qc + (j0 - c0));
+#pragma unroll
+            for (int e = 0; e < kDrawPerThread; e += 4) {
+                const uint4 v = src[e / 4];
+                qv[e] = __uint_as_float(v.x); qv[e + 1] = __uint_as_float(v.y);
+                qv[e + 2] = __uint_as_float(v.z); qv[e + 3] = __uint_as_float(v.w);
+            }
+        }
+    } else if (has_q) {
+        load16(d.qrow, j0, d.V, qv);
+    }
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) {
         const bool in = j0 + e < d.V;
         p[e] = in ? target_prob(l[e], d.M, d.S) : 0.f;
-        w[e] = in ? (d.qrow ? fmaxf(0.f, p[e] - qv[e]) : p[e]) : 0.f;
+        w[e] = in ? (has_q ? fmaxf(0.f, p[e] - qv[e]) : p[e]) : 0.f;
     }
 }
 
 // The inverse-CDF draw for sequence b from its chunk totals.  Returns the
 // token; *flags gets SV_DEV_FALLBACK / SV_DEV_NONFINITE.
+template <bool SPARSE>
 __device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* psum, float u,
-                    int* flags) {
+                    unsigned* s_qc, int* flags) {
     __shared__ double s_before;
     // Thread t owns chunks [t*per, (t+1)*per) of the chunk totals.
     const int per = (NC + kBlock - 1) / kBlock;
@@ -247,7 +400,7 @@ __device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* 
     *flags = 0;
     if (!(S > 0.0)) {
         *flags = SV_DEV_FALLBACK;
-        d.qrow = nullptr;
+        d.drop_q();
         sums = psum + (size_t)b * NC;
         own = 0.0;
         for (int c = c0; c < c1; ++c) own += sums[c];
@@ -281,9 +434,11 @@ __device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* 
     const double before = s_before;
 
     // Rescan that chunk in token order.
-    const int j0 = chunk * kDrawChunk + threadIdx.x * kDrawPerThread;
+    const int cs = chunk * kDrawChunk;
+    if (SPARSE && d.has_q()) stage_sparse_chunk(d, cs, s_qc);
+    const int j0 = cs + threadIdx.x * kDrawPerThread;
     float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights16(d, j0, w, p);
+    draw_weights16<SPARSE>(d, j0, s_qc, cs, w, p);
     double mine = 0.0, chunk_total;
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) mine += (double)w[e];
@@ -305,18 +460,19 @@ __device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* 
 
 // Accept tests once per sequence (the split form, for many sequences):
 // n, the row normalisers, the kept drafts, padding and status.
+template <bool SPARSE>
 __global__ __launch_bounds__(kBlock) void accept_kernel(
     const float* __restrict__ logits, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
-    const float* __restrict__ q, const float* __restrict__ uniforms, int gamma, int V,
+    QArg q, const float* __restrict__ uniforms, int gamma, int V,
     float* __restrict__ row_max, float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
     __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
     const int b = blockIdx.x;
     const int g1 = gamma + 1;
-    bool bad;
-    const int n = accept_tests(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q, uniforms,
-                               r_m, r_s, &bad);
+    int flags;
+    const int n = accept_tests<SPARSE>(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q,
+                                       uniforms, r_m, r_s, &flags);
     if (threadIdx.x < g1) {
         const int i = threadIdx.x;
         row_max[(size_t)b * g1 + i] = r_m[i];
@@ -325,7 +481,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(
     }
     if (threadIdx.x == 0) {
         n_accepted[b] = n;
-        status[b] = bad ? SV_DEV_BAD_DRAFT : 0;
+        status[b] = flags;
     }
 }
 
@@ -334,26 +490,27 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(
 // Otherwise accept_kernel ran first, the workgroup reads n and the draw
 // row's normaliser it left, only writes its chunk totals, and pick_kernel
 // follows: the kernel boundary orders the totals before the pick.
-template <bool FUSED>
+template <bool FUSED, bool SPARSE>
 __global__ __launch_bounds__(kBlock) void draw_kernel(
     const float* __restrict__ logits, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
-    const float* __restrict__ q, const float* __restrict__ uniforms, int gamma, int V, int NC,
+    QArg q, const float* __restrict__ uniforms, int gamma, int V, int NC,
     double* __restrict__ csum, double* __restrict__ psum, int32_t* __restrict__ counters,
     float* __restrict__ row_max, float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
     __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
+    __shared__ __attribute__((aligned(16))) unsigned s_qc[SPARSE ? kDrawChunk : 4];
     __shared__ int s_last;
     // flat grid: workgroup x covers chunk x % NC of sequence x / NC
     const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
     const int g1 = gamma + 1;
 
-    bool bad = false;
+    int flags = 0;
     int n;
     float M, S;
     if (FUSED) {
-        n = accept_tests(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q, uniforms,
-                         r_m, r_s, &bad);
+        n = accept_tests<SPARSE>(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q,
+                                 uniforms, r_m, r_s, &flags);
         M = r_m[n];
         S = r_s[n];
     } else {
@@ -361,16 +518,12 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
         M = row_max[(size_t)b * g1 + n];
         S = row_sum[(size_t)b * g1 + n];
     }
-    const size_t k = (size_t)b * g1 + n;
-    DrawRow d;
-    d.lrow = logits + k * V;
-    d.qrow = n < gamma ? q + ((size_t)b * gamma + n) * V : nullptr;
-    d.M = M;
-    d.S = S;
-    d.V = V;
+    const DrawRow d = draw_row<SPARSE>(logits, q, b, gamma, n, V, M, S);
+    const int cs = c * kDrawChunk;
+    if (SPARSE && d.has_q()) stage_sparse_chunk(d, cs, s_qc);
 
     float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights16(d, c * kDrawChunk + threadIdx.x * kDrawPerThread, w, p);
+    draw_weights16<SPARSE>(d, cs + threadIdx.x * kDrawPerThread, s_qc, cs, w, p);
     double tw = 0.0, tp = 0.0;
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
@@ -398,35 +551,32 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
         if (i != n) out_tokens[(size_t)b * g1 + i] = i < n ? draft[(size_t)b * gamma + i] : -1;
     }
     // ... and the draw.
-    int flags;
-    const int tok = pick(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], &flags);
+    int pflags;
+    const int tok = pick<SPARSE>(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], s_qc, &pflags);
     if (threadIdx.x == 0) {
-        out_tokens[k] = tok;
+        out_tokens[(size_t)b * g1 + n] = tok;
         n_accepted[b] = n;
-        status[b] = (bad ? SV_DEV_BAD_DRAFT : 0) | flags;
+        status[b] = flags | pflags;
         counters[b] = 0;                       // ready for a repeated stage-2 call
     }
 }
 
 // The draw for one sequence from the chunk totals draw_kernel<false> wrote.
+template <bool SPARSE>
 __global__ __launch_bounds__(kBlock) void pick_kernel(
-    const float* __restrict__ logits, const float* __restrict__ q,
+    const float* __restrict__ logits, QArg q,
     const float* __restrict__ uniforms, int gamma, int V, int NC, const double* __restrict__ csum,
     const double* __restrict__ psum, const float* __restrict__ row_max,
     const float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
     const int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
+    __shared__ __attribute__((aligned(16))) unsigned s_qc[SPARSE ? kDrawChunk : 4];
     const int b = blockIdx.x;
     const int g1 = gamma + 1;
     const int n = n_accepted[b];
     const size_t k = (size_t)b * g1 + n;
-    DrawRow d;
-    d.lrow = logits + k * V;
-    d.qrow = n < gamma ? q + ((size_t)b * gamma + n) * V : nullptr;
-    d.M = row_max[k];
-    d.S = row_sum[k];
-    d.V = V;
+    const DrawRow d = draw_row<SPARSE>(logits, q, b, gamma, n, V, row_max[k], row_sum[k]);
     int flags;
-    const int tok = pick(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], &flags);
+    const int tok = pick<SPARSE>(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], s_qc, &flags);
     if (threadIdx.x == 0) {
         out_tokens[k] = tok;
         if (flags) status[b] |= flags;
@@ -439,37 +589,59 @@ __global__ __launch_bounds__(kBlock) void pick_kernel(
 #define SV_FUSE_MAX_GROUPS 64
 #endif
 
-hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
-                              int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
-                              const float* q, const float* uniforms, int NC, double* csum,
-                              double* psum, int32_t* counters, float* row_max, float* row_sum,
-                              int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
-                              hipStream_t stream) {
+namespace {
+
+template <bool SPARSE>
+hipError_t launch_accept_draw_t(const float* logits, const float* part_max, const float* part_sum,
+                                int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
+                                QArg q, const float* uniforms, int NC, double* csum, double* psum,
+                                int32_t* counters, float* row_max, float* row_sum,
+                                int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
+                                hipStream_t stream) {
     const unsigned groups = (unsigned)NC * (unsigned)B;
     // Few draw workgroups: fuse the accept tests into each and let the last
     // one pick (one launch).  Many: accept once per sequence, chunk totals,
     // then the pick -- three launches, no workgroup repeats the accept tests
     // and none waits on a device-wide fence.
     if (groups <= SV_FUSE_MAX_GROUPS) {
-        draw_kernel<true><<<dim3(groups), dim3(kBlock), 0, stream>>>(
+        draw_kernel<true, SPARSE><<<dim3(groups), dim3(kBlock), 0, stream>>>(
             logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum,
             counters, row_max, row_sum, out_tokens, n_accepted, status);
         return hipGetLastError();
     }
-    accept_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(logits, part_max, part_sum, NP, NPs, draft, q,
-                                                       uniforms, gamma, V, row_max, row_sum,
-                                                       out_tokens, n_accepted, status);
+    accept_kernel<SPARSE><<<dim3(B), dim3(kBlock), 0, stream>>>(
+        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, row_max, row_sum,
+        out_tokens, n_accepted, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    draw_kernel<false><<<dim3(groups), dim3(kBlock), 0, stream>>>(
+    draw_kernel<false, SPARSE><<<dim3(groups), dim3(kBlock), 0, stream>>>(
         logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum,
         counters, row_max, row_sum, out_tokens, n_accepted, status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    pick_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(logits, q, uniforms, gamma, V, NC, csum, psum,
-                                                     row_max, row_sum, out_tokens, n_accepted,
-                                                     status);
+    pick_kernel<SPARSE><<<dim3(B), dim3(kBlock), 0, stream>>>(logits, q, uniforms, gamma, V, NC,
+                                                             csum, psum, row_max, row_sum,
+                                                             out_tokens, n_accepted, status);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// q_idx == nullptr: dense q [B][gamma][V]; otherwise sparse q, K entries per row.
+hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
+                              int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
+                              const float* q, const int32_t* q_idx, int K, const float* uniforms,
+                              int NC, double* csum, double* psum, int32_t* counters,
+                              float* row_max, float* row_sum, int32_t* out_tokens,
+                              int32_t* n_accepted, int32_t* status, hipStream_t stream) {
+    const QArg qa{q, q_idx, K};
+    if (q_idx)
+        return launch_accept_draw_t<true>(logits, part_max, part_sum, NP, NPs, B, gamma, V, draft,
+                                          qa, uniforms, NC, csum, psum, counters, row_max, row_sum,
+                                          out_tokens, n_accepted, status, stream);
+    return launch_accept_draw_t<false>(logits, part_max, part_sum, NP, NPs, B, gamma, V, draft, qa,
+                                       uniforms, NC, csum, psum, counters, row_max, row_sum,
+                                       out_tokens, n_accepted, status, stream);
 }
 
 }  // namespace sv

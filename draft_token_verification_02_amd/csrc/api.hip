@@ -18,9 +18,13 @@ hipError_t launch_greedy(const float* part_max, const int32_t* part_arg, int NP,
                          hipStream_t stream);
 hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
                               int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
-                              const float* q, const float* uniforms, int NC, double* csum,
-                              double* psum, int32_t* counters, float* row_max, float* row_sum,
-                              int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
+                              const float* q, const int32_t* q_idx, int K, const float* uniforms,
+                              int NC, double* csum, double* psum, int32_t* counters,
+                              float* row_max, float* row_sum, int32_t* out_tokens,
+                              int32_t* n_accepted, int32_t* status, hipStream_t stream);
+hipError_t launch_sparse_head(const uint16_t* h, const uint16_t* W, const uint16_t* cent,
+                              const int32_t* members, int N, int d, int V, int C, int M, int k,
+                              int32_t* q_ids, float* q_vals, int32_t* clusters, void* ws,
                               hipStream_t stream);
 }  // namespace sv
 
@@ -81,15 +85,17 @@ sv_status stage2_greedy(const int32_t* draft, sv_dims dims, int32_t* out_tokens,
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
-sv_status stage2(const int32_t* draft, const float* q, const float* uniforms, sv_dims dims,
-                 int32_t* out_tokens, int32_t* n_accepted, void* ws, hipStream_t s) {
+// q_idx == nullptr: dense q [B][gamma][V]; otherwise sparse q with K entries per row.
+sv_status stage2(const int32_t* draft, const float* q, const int32_t* q_idx, int K,
+                 const float* uniforms, sv_dims dims, int32_t* out_tokens, int32_t* n_accepted,
+                 void* ws, hipStream_t s) {
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     hipError_t e = sv::launch_accept_draw(
         at<float>(ws, L.logits), at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
-        lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.gamma, dims.V, draft, q, uniforms, L.NC,
-        at<double>(ws, L.csum), at<double>(ws, L.psum), at<int32_t>(ws, L.counters),
-        at<float>(ws, L.row_max), at<float>(ws, L.row_sum), out_tokens, n_accepted,
-        at<int32_t>(ws, L.status), s);
+        lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.gamma, dims.V, draft, q, q_idx, K,
+        uniforms, L.NC, at<double>(ws, L.csum), at<double>(ws, L.psum),
+        at<int32_t>(ws, L.counters), at<float>(ws, L.row_max), at<float>(ws, L.row_sum),
+        out_tokens, n_accepted, at<int32_t>(ws, L.status), s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
@@ -110,6 +116,24 @@ sv_status check_stage2(const int32_t* draft, const float* q, const float* unifor
         !aligned(n_accepted, 4))
         return SV_ERR_ALIGN;
     return check_workspace(ws, bytes, dims);
+}
+
+sv_status check_stage2_sparse(const int32_t* draft, const int32_t* q_ids, const float* q_vals,
+                              int32_t K, const float* uniforms, sv_dims dims,
+                              const int32_t* out_tokens, const int32_t* n_accepted, const void* ws,
+                              size_t bytes) {
+    if (!dims_ok(dims) || K < 1 || K > (1 << 24)) return SV_ERR_DIMS;
+    if (!draft || !q_ids || !q_vals || !uniforms || !out_tokens || !n_accepted) return SV_ERR_NULL;
+    if (!aligned(q_ids, 16) || !aligned(q_vals, 16) || !aligned(draft, 4) || !aligned(uniforms, 4) ||
+        !aligned(out_tokens, 4) || !aligned(n_accepted, 4))
+        return SV_ERR_ALIGN;
+    return check_workspace(ws, bytes, dims);
+}
+
+bool head_dims_ok(sv_head_dims d) {
+    return d.N >= 1 && d.N <= 65535 && d.d >= 8 && d.d <= 65536 && d.d % 8 == 0 && d.V >= 1 &&
+           d.V <= (1 << 28) && d.C >= 1 && d.C <= SV_HEAD_MAX_CLUSTERS && d.M >= 1 && d.k >= 1 &&
+           d.k <= d.C && (int64_t)d.k * d.M <= (1 << 24);
 }
 
 sv_status check_greedy(const int32_t* draft, sv_dims dims, const int32_t* out_tokens,
@@ -159,7 +183,7 @@ sv_status sv_accept_and_draw(const int32_t* draft_tokens, const float* q, const 
     const sv_status st = check_stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted,
                                       workspace, workspace_bytes);
     if (st != SV_OK) return st;
-    return stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace,
+    return stage2(draft_tokens, q, nullptr, 0, uniforms, dims, out_tokens, n_accepted, workspace,
                   static_cast<hipStream_t>(hip_stream));
 }
 
@@ -173,7 +197,59 @@ sv_status spec_verify(const uint16_t* hidden, const uint16_t* W_lmhead, const in
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     st = stage1(hidden, W_lmhead, dims, workspace, s);
     if (st != SV_OK) return st;
-    return stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace, s);
+    return stage2(draft_tokens, q, nullptr, 0, uniforms, dims, out_tokens, n_accepted, workspace, s);
+}
+
+sv_status sv_accept_and_draw_sparse_q(const int32_t* draft_tokens, const int32_t* q_ids,
+                                      const float* q_vals, int32_t K, const float* uniforms,
+                                      sv_dims dims, int32_t* out_tokens, int32_t* n_accepted,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const sv_status st = check_stage2_sparse(draft_tokens, q_ids, q_vals, K, uniforms, dims,
+                                             out_tokens, n_accepted, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    return stage2(draft_tokens, q_vals, q_ids, K, uniforms, dims, out_tokens, n_accepted,
+                  workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+sv_status spec_verify_sparse_q(const uint16_t* hidden, const uint16_t* W_lmhead,
+                               const int32_t* draft_tokens, const int32_t* q_ids,
+                               const float* q_vals, int32_t K, const float* uniforms,
+                               sv_dims dims, int32_t* out_tokens, int32_t* n_accepted,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+    sv_status st = check_stage1(hidden, W_lmhead, dims, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    st = check_stage2_sparse(draft_tokens, q_ids, q_vals, K, uniforms, dims, out_tokens,
+                             n_accepted, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = stage1(hidden, W_lmhead, dims, workspace, s);
+    if (st != SV_OK) return st;
+    return stage2(draft_tokens, q_vals, q_ids, K, uniforms, dims, out_tokens, n_accepted,
+                  workspace, s);
+}
+
+size_t sv_sparse_head_workspace_bytes(sv_head_dims dims) {
+    if (!head_dims_ok(dims)) return 0;
+    return sv::make_head_layout(dims.N, dims.C, dims.k * dims.M).total;
+}
+
+sv_status sv_sparse_head(const uint16_t* h, const uint16_t* W_lmhead, const uint16_t* centroids,
+                         const int32_t* members, sv_head_dims dims, int32_t* q_ids, float* q_vals,
+                         int32_t* clusters, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+    if (!head_dims_ok(dims)) return SV_ERR_DIMS;
+    if (!h || !W_lmhead || !centroids || !members || !q_ids || !q_vals || !workspace)
+        return SV_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(W_lmhead, 16) || !aligned(centroids, 16) ||
+        !aligned(members, 4) || !aligned(q_ids, 4) || !aligned(q_vals, 4) ||
+        !aligned(clusters, 4) || !aligned(workspace, 256))
+        return SV_ERR_ALIGN;
+    if (workspace_bytes < sv_sparse_head_workspace_bytes(dims)) return SV_ERR_WORKSPACE;
+    const hipError_t e = sv::launch_sparse_head(h, W_lmhead, centroids, members, dims.N, dims.d,
+                                                dims.V, dims.C, dims.M, dims.k, q_ids, q_vals,
+                                                clusters, workspace,
+                                                static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
 sv_status sv_accept_greedy(const int32_t* draft_tokens, sv_dims dims, int32_t* out_tokens,

@@ -1,0 +1,378 @@
+// The drafter's clustered sparse LM head: q over the tokens of the k best
+// clusters only, exactly 0 elsewhere.
+//
+// Source: "多詞元預測視覺化指南" (gemma.gh.miniasp.com), section 高效嵌入器:
+// the tokens' embeddings are grouped into clusters, each with an embedding of
+// its own; the hidden state times that small table gives one logit per
+// cluster, the most likely clusters are chosen, and token logits are formed
+// only for the tokens of the chosen clusters.  q is their softmax.
+//
+// Four launches, N hidden rows (one per drafted position):
+//   scores_kernel  cluster logits h . centroid^T, [N][C] fp32.  The table is
+//                  small (C x d bf16, 6 MB at C = 2048, d = 1536), so each
+//                  workgroup takes 16 centroids and splits k over its waves
+//                  (v_mfma_f32_16x16x32_bf16, centroids as A, hidden rows as
+//                  B), summed through LDS in wave order: C / 16 workgroups
+//                  all streaming at once instead of a few long ones.
+//   topk_kernel    per row, the k largest cluster logits (ties to the lower
+//                  cluster id) by an exact 4-pass radix select on order-
+//                  preserving keys, then the chosen clusters in ascending id
+//                  and their members in the members table's order: the
+//                  row's K = k * M token ids.
+//   gather_kernel  token logits h . W[id] for the K ids of each row: W rows
+//                  gathered straight into the MFMA A operand (16 tokens per
+//                  fragment, 16 contiguous bytes per lane), the hidden row as
+//                  B; one softmax partial (max, sum exp) per workgroup.
+//   qfinal_kernel  q = exp(l - max) / sum exp from the row's partials.
+// Member ids outside [0, V) are dropped: their slots hold id -1 (the padding
+// id of the sparse-q verify entry points) and q = 0.
+
+#include "sv_common.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kSplit = 4;            // waves splitting k in scores_kernel
+constexpr int kGT = 2;               // 16-token fragments per wave in gather_kernel
+constexpr int kGWaves = 4;           // waves per gather workgroup
+constexpr int kGU = 8;               // k-steps loaded per batch in gather_kernel
+
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ __launch_bounds__(kSplit * kWave) void scores_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ cent, int N, int d, int C,
+    float* __restrict__ scores) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int c0 = blockIdx.x * kLmTile;
+    const int n0 = blockIdx.y * kLmTile * MT;
+
+    const uint16_t* ap = cent + (size_t)min(c0 + r16, C - 1) * d + kg * 8;
+    const uint16_t* bp[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) bp[m] = h + (size_t)min(n0 + m * kLmTile + r16, N - 1) * d + kg * 8;
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nstep = (d + 31) / 32;
+#pragma unroll 4
+    for (int ks = wave; ks < nstep; ks += kSplit) {
+        const bool ok = ks * 32 + kg * 8 < d;          // d is a multiple of 8
+        const u32x4 zero{0u, 0u, 0u, 0u};
+        const u32x4 a = ok ? *reinterpret_cast<const u32x4*>(ap + ks * 32) : zero;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const u32x4 b = ok ? *reinterpret_cast<const u32x4*>(bp[m] + ks * 32) : zero;
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m], 0, 0, 0);
+        }
+    }
+
+    __shared__ f32x4 red[kSplit][MT][kWave];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            f32x4 s = red[0][m][lane];
+#pragma unroll
+            for (int w = 1; w < kSplit; ++w) s += red[w][m][lane];
+            // lane holds D[centroid 4*kg + i][hidden row r16] of fragment m
+            const int n = n0 + m * kLmTile + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + 4 * kg + i;
+                if (n < N && c < C) scores[(size_t)n * C + c] = s[i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup-wide integer scans in a fixed order.
+__device__ int block_inclusive_scan_int(int v, int* total) {
+    __shared__ int s_wave[kBlock / kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) s_wave[wave] = v;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) {
+        if (w < wave) before += s_wave[w];
+        all += s_wave[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + v;
+}
+
+__device__ __forceinline__ int block_exclusive_scan_int(int v) {
+    int total;
+    return block_inclusive_scan_int(v, &total) - v;
+}
+
+// A key whose unsigned order is the float order (-0 and +0 equal, NaN lowest).
+__device__ __forceinline__ unsigned order_key(float f) {
+    if (f != f) return 0u;
+    if (f == 0.f) f = 0.f;
+    const unsigned u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(kBlock) void topk_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ members, int C, int M, int k,
+    int V, int32_t* __restrict__ q_ids, int32_t* __restrict__ clusters) {
+    __shared__ unsigned s_key[SV_HEAD_MAX_CLUSTERS];
+    __shared__ int s_sel[SV_HEAD_MAX_CLUSTERS];
+    __shared__ int s_hist[256];
+    __shared__ int s_digit, s_above;
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x;
+    const float* row = scores + (size_t)n * C;
+    for (int c = tid; c < C; c += kBlock) {
+        s_key[c] = order_key(row[c]);
+        s_sel[c] = -1;
+    }
+
+    // The k-th largest key, 8 bits at a time from the top: at each pass count
+    // the keys that match the digits found so far by their next digit, and
+    // take the digit where the count of keys at or above it reaches the
+    // number still needed.
+    unsigned prefix = 0u, pmask = 0u;
+    int need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        s_hist[tid] = 0;
+        __syncthreads();
+        for (int c = tid; c < C; c += kBlock) {
+            const unsigned key = s_key[c];
+            if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        const int v = s_hist[255 - tid];             // digits from the top
+        int total;
+        const int at_or_above = block_inclusive_scan_int(v, &total);
+        if (at_or_above >= need && at_or_above - v < need) {
+            s_digit = 255 - tid;
+            s_above = at_or_above - v;
+        }
+        __syncthreads();
+        prefix |= (unsigned)s_digit << shift;
+        pmask |= 255u << shift;
+        need -= s_above;
+        __syncthreads();
+    }
+    // Chosen: every key above the threshold, and the first `need` keys equal
+    // to it in cluster order.  Thread t owns clusters [t*per, (t+1)*per).
+    const int per = (C + kBlock - 1) / kBlock;
+    const int cb = tid * per, ce = min(C, cb + per);
+    int neq = 0;
+    for (int c = cb; c < ce; ++c) neq += s_key[c] == prefix;
+    const int eq_before = block_exclusive_scan_int(neq);
+    auto chosen = [&](int c, int& eqs) {
+        const unsigned key = s_key[c];
+        if (key > prefix) return true;
+        if (key == prefix) return eqs++ < need;
+        return false;
+    };
+    int nsel = 0, eqs = eq_before;
+    for (int c = cb; c < ce; ++c) nsel += chosen(c, eqs);
+    int pos = block_exclusive_scan_int(nsel);
+    eqs = eq_before;
+    for (int c = cb; c < ce; ++c)
+        if (chosen(c, eqs)) s_sel[pos++] = c;
+    __syncthreads();
+
+    if (clusters)
+        for (int j = tid; j < k; j += kBlock) clusters[(size_t)n * k + j] = s_sel[j];
+    const int K = k * M;
+    int32_t* out = q_ids + (size_t)n * K;
+    for (int e = tid; e < K; e += kBlock) {
+        const int j = e / M, m = e - j * M;
+        const int c = s_sel[j];                 // always a chosen cluster; -1 never read
+        const int id = c >= 0 ? members[(size_t)c * M + m] : -1;
+        out[e] = id >= 0 && id < V ? id : -1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kGWaves * kWave) void gather_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ q_ids, int K, int d, float* __restrict__ tl,
+    float* __restrict__ pmax, float* __restrict__ psum, int G) {
+    constexpr int kTok = kGT * kLmTile;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int n = blockIdx.y;
+    const int tok0 = (blockIdx.x * kGWaves + wave) * kTok;
+    const int32_t* ids = q_ids + (size_t)n * K;
+
+    // A rows: the gathered W rows of this lane's fragment row (padding and
+    // dropped ids read row 0; their results are discarded).
+    const uint16_t* ap[kGT];
+#pragma unroll
+    for (int t = 0; t < kGT; ++t) {
+        const int j = tok0 + t * kLmTile + r16;
+        const int id = j < K ? ids[j] : -1;
+        ap[t] = W + (size_t)(id >= 0 ? id : 0) * d + kg * 8;
+    }
+    // B: the hidden row in every column.
+    const uint16_t* bp = h + (size_t)n * d + kg * 8;
+
+    f32x4 acc[kGT];
+#pragma unroll
+    for (int t = 0; t < kGT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nstep = (d + 31) / 32;
+    const u32x4 zero{0u, 0u, 0u, 0u};
+    for (int ks0 = 0; ks0 < nstep; ks0 += kGU) {
+        u32x4 a[kGU][kGT], b[kGU];
+#pragma unroll
+        for (int u = 0; u < kGU; ++u) {
+            const int ks = ks0 + u;
+            const bool ok = ks < nstep && ks * 32 + kg * 8 < d;
+#pragma unroll
+            for (int t = 0; t < kGT; ++t)
+                a[u][t] = ok ? *reinterpret_cast<const u32x4*>(ap[t] + ks * 32) : zero;
+            b[u] = ok ? *reinterpret_cast<const u32x4*>(bp + ks * 32) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < kGU; ++u)
+#pragma unroll
+            for (int t = 0; t < kGT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a[u][t]), __builtin_bit_cast(bf16x8, b[u]), acc[t],
+                    0, 0, 0);
+    }
+
+    // Lane (r16, kg) holds D[token 4*kg + i][column r16]; the columns are
+    // equal, so column 0's lanes write.  Their running (max, sum exp).
+    float m = -INFINITY, s = 0.f;
+    if (r16 == 0) {
+        float v[kGT][4];
+#pragma unroll
+        for (int t = 0; t < kGT; ++t) {
+            const int j0 = tok0 + t * kLmTile + 4 * kg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = j0 + i;
+                const bool live = j < K && ids[j] >= 0;
+                v[t][i] = live ? acc[t][i] : -INFINITY;
+                if (j < K) tl[(size_t)n * K + j] = v[t][i];
+                m = fmaxf(m, v[t][i]);
+            }
+        }
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int t = 0; t < kGT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (v[t][i] != -INFINITY) s += expf(v[t][i] - m);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+        lse_merge(m, s, m2, s2);
+    }
+    __shared__ float s_m[kGWaves], s_s[kGWaves];
+    if (lane == 0) { s_m[wave] = m; s_s[wave] = s; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float mm = -INFINITY, ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGWaves; ++w) lse_merge(mm, ss, s_m[w], s_s[w]);
+        pmax[(size_t)n * G + blockIdx.x] = mm;
+        psum[(size_t)n * G + blockIdx.x] = ss;
+    }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kQPer = 4;                       // values per thread in qfinal_kernel
+
+__global__ __launch_bounds__(kBlock) void qfinal_kernel(
+    const float* __restrict__ tl, const float* __restrict__ pmax, const float* __restrict__ psum,
+    int G, int K, float* __restrict__ q_vals) {
+    __shared__ float s_m, s_s;
+    const int n = blockIdx.y;
+    if (threadIdx.x < kWave) {
+        float m = -INFINITY, s = 0.f;
+        for (int g = threadIdx.x; g < G; g += kWave)
+            lse_merge(m, s, pmax[(size_t)n * G + g], psum[(size_t)n * G + g]);
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+            lse_merge(m, s, m2, s2);
+        }
+        if (threadIdx.x == 0) { s_m = m; s_s = s; }
+    }
+    __syncthreads();
+    const float m = s_m, s = s_s;
+    const int j1 = min(K, (int)(blockIdx.x + 1) * kBlock * kQPer);
+    for (int j = blockIdx.x * kBlock * kQPer + threadIdx.x; j < j1; j += kBlock) {
+        const float l = tl[(size_t)n * K + j];
+        q_vals[(size_t)n * K + j] = s > 0.f && l != -INFINITY ? expf(l - m) / s : 0.f;
+    }
+}
+
+}  // namespace
+
+// Workspace of the sparse head: cluster scores [N][C], token logits [N][K],
+// gather partials (max, sum exp) [N][G] each.
+HeadLayout make_head_layout(int N, int C, int K) {
+    HeadLayout L;
+    L.G = (K + kGT * kLmTile * kGWaves - 1) / (kGT * kLmTile * kGWaves);
+    size_t off = 0;
+    L.scores = off; off = align_up(off + (size_t)N * C * sizeof(float), 256);
+    L.tl = off;     off = align_up(off + (size_t)N * K * sizeof(float), 256);
+    L.pmax = off;   off = align_up(off + (size_t)N * L.G * sizeof(float), 256);
+    L.psum = off;   off = align_up(off + (size_t)N * L.G * sizeof(float), 256);
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_sparse_head(const uint16_t* h, const uint16_t* W, const uint16_t* cent,
+                              const int32_t* members, int N, int d, int V, int C, int M, int k,
+                              int32_t* q_ids, float* q_vals, int32_t* clusters, void* ws,
+                              hipStream_t stream) {
+    const int K = k * M;
+    const HeadLayout L = make_head_layout(N, C, K);
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base + L.scores);
+    float* tl = reinterpret_cast<float*>(base + L.tl);
+    float* pmax = reinterpret_cast<float*>(base + L.pmax);
+    float* psum = reinterpret_cast<float*>(base + L.psum);
+
+    const int ctiles = (C + kLmTile - 1) / kLmTile;
+    const int mt = N <= 16 ? 1 : N <= 32 ? 2 : N <= 48 ? 3 : 4;
+    const dim3 sg(ctiles, (N + kLmTile * mt - 1) / (kLmTile * mt)), sb(kSplit * kWave);
+    switch (mt) {
+        case 1: scores_kernel<1><<<sg, sb, 0, stream>>>(h, cent, N, d, C, scores); break;
+        case 2: scores_kernel<2><<<sg, sb, 0, stream>>>(h, cent, N, d, C, scores); break;
+        case 3: scores_kernel<3><<<sg, sb, 0, stream>>>(h, cent, N, d, C, scores); break;
+        default: scores_kernel<4><<<sg, sb, 0, stream>>>(h, cent, N, d, C, scores); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    topk_kernel<<<dim3(N), dim3(kBlock), 0, stream>>>(scores, members, C, M, k, V, q_ids, clusters);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    gather_kernel<<<dim3(L.G, N), dim3(kGWaves * kWave), 0, stream>>>(h, W, q_ids, K, d, tl, pmax,
+                                                                    psum, L.G);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    qfinal_kernel<<<dim3((K + kBlock * kQPer - 1) / (kBlock * kQPer), N), dim3(kBlock), 0, stream>>>(
+        tl, pmax, psum, L.G, K, q_vals);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -78,6 +78,14 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     return L;
 }
 
+// Byte offsets inside the workspace of the drafter's sparse head
+// (make_head_layout, in sparse_head.hip).
+struct HeadLayout {
+    int G;                    // gather workgroups (softmax partials) per row
+    size_t scores, tl, pmax, psum, total;
+};
+HeadLayout make_head_layout(int N, int C, int K);
+
 // Merge of two (max, sum of exp(x - max)) pairs: the online-softmax step.
 // Symmetric in its two arguments, so a butterfly gives every lane the same bits.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {

@@ -56,7 +56,7 @@ extern "C" {
 #define SV_API
 #endif
 
-#define SV_ABI_VERSION 2
+#define SV_ABI_VERSION 3
 #define SV_MAX_GAMMA 32
 
 typedef struct {
@@ -80,6 +80,7 @@ typedef enum {
 #define SV_DEV_FALLBACK 2   /* the residual summed to <= 0; the replacement was drawn from p */
 #define SV_DEV_NONFINITE 4  /* no finite positive weights at all (greedy: no logit above
                                -inf in the emitting row); token 0 was emitted */
+#define SV_DEV_BAD_QID 8    /* a sparse q row listed an id >= V (the entry was ignored) */
 
 /* ABI version of the loaded library (SV_ABI_VERSION). */
 SV_API int32_t sv_abi_version(void);
@@ -146,6 +147,76 @@ SV_API sv_status spec_verify_greedy(const uint16_t *hidden, const uint16_t *W_lm
 SV_API sv_status sv_accept_greedy(const int32_t *draft_tokens, sv_dims dims, int32_t *out_tokens,
                            int32_t *n_accepted, int32_t *target_tokens, void *workspace,
                            size_t workspace_bytes, void *hip_stream);
+
+/* Verification with the drafter's q given sparsely: K (id, value) entries
+ * per drafted position instead of a dense [V] row.  The result is that of
+ * spec_verify on the dense row holding those values at those ids and 0
+ * elsewhere -- the form a clustered drafter head produces, whose q is exactly
+ * 0 outside its chosen clusters ("多詞元預測視覺化指南", section 高效嵌入器;
+ * the rule itself: "推测解码", section 通过的规则).  Only the K entries of a
+ * row are read, never V floats.
+ *   q_ids   int32 [B][gamma][K]  token ids, in any order; ids < 0 are padding
+ *                                (a row with fewer entries pads with -1);
+ *                                ids >= V are ignored and set SV_DEV_BAD_QID
+ *   q_vals  fp32  [B][gamma][K]  q at those ids; negative and NaN values count
+ *                                as 0; an id listed twice takes the larger value
+ *   K       entries per row, 1 <= K <= 2^24
+ * Other arguments and the workspace as for spec_verify.  q_ids and q_vals
+ * must be 16-byte aligned. */
+SV_API sv_status spec_verify_sparse_q(const uint16_t *hidden, const uint16_t *W_lmhead,
+                               const int32_t *draft_tokens, const int32_t *q_ids,
+                               const float *q_vals, int32_t K, const float *uniforms,
+                               sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
+                               void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Stage 2 of spec_verify_sparse_q alone, after sv_lmhead on the same
+ * workspace, dims and device. */
+SV_API sv_status sv_accept_and_draw_sparse_q(const int32_t *draft_tokens, const int32_t *q_ids,
+                                      const float *q_vals, int32_t K, const float *uniforms,
+                                      sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *hip_stream);
+
+/* ------------------------------------------------------------------------
+ * The drafter's clustered sparse LM head, which produces that sparse q
+ * ("多詞元預測視覺化指南", section 高效嵌入器): the vocabulary is grouped into C
+ * clusters of M tokens, each cluster with an embedding of its own.  For each
+ * of N hidden rows h:
+ *   1. score[c] = h . centroids[c] for every cluster (fp32);
+ *   2. the k clusters with the largest scores are chosen (ties to the lower
+ *      cluster id), listed in ascending cluster id;
+ *   3. the row's K = k*M token ids are the chosen clusters' members, cluster
+ *      by cluster in that order, each cluster's in the members table's order;
+ *   4. logit[j] = h . W[id_j] and q = softmax over those K logits (fp32).
+ * Members outside [0, V) are dropped: their slots get id -1 and q = 0. */
+#define SV_HEAD_MAX_CLUSTERS 8192
+
+typedef struct {
+    int32_t N;   /* hidden rows, 1..65535 */
+    int32_t d;   /* hidden size, 8..65536, a multiple of 8 */
+    int32_t V;   /* vocabulary size (rows of W), 1..2^28 */
+    int32_t C;   /* clusters, 1..SV_HEAD_MAX_CLUSTERS */
+    int32_t M;   /* tokens per cluster (width of the members table), >= 1 */
+    int32_t k;   /* clusters chosen per row, 1..C; k*M <= 2^24 */
+} sv_head_dims;
+
+/* Device workspace bytes of sv_sparse_head (0 if dims are invalid). */
+SV_API size_t sv_sparse_head_workspace_bytes(sv_head_dims dims);
+
+/*   h          bf16 bits [N][d]   drafter hidden states
+ *   W_lmhead   bf16 bits [V][d]   the tied embedding table (as for spec_verify)
+ *   centroids  bf16 bits [C][d]   one embedding per cluster
+ *   members    int32 [C][M]       token ids of each cluster
+ *   q_ids      int32 [N][k*M]     out: the row's token ids (step 3)
+ *   q_vals     fp32  [N][k*M]     out: q at those ids
+ *   clusters   int32 [N][k]       out, may be NULL: the chosen clusters
+ * h, W_lmhead and centroids must be 16-byte aligned, the workspace 256-byte
+ * aligned.  Conventions as for the entry points above.  The outputs feed
+ * spec_verify_sparse_q directly (N = B*gamma rows, K = k*M). */
+SV_API sv_status sv_sparse_head(const uint16_t *h, const uint16_t *W_lmhead,
+                         const uint16_t *centroids, const int32_t *members, sv_head_dims dims,
+                         int32_t *q_ids, float *q_vals, int32_t *clusters, void *workspace,
+                         size_t workspace_bytes, void *hip_stream);
 
 /* Device pointers into `workspace` for inspection after a call completes:
  *   logits      fp32 [R][V]

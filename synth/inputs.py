@@ -294,3 +294,116 @@ def iid_positions(V: int, d: int, gamma: int, n: int, seed: int, *, sigma: float
     draft = np.argmax(keys, axis=-1).astype(np.int32)
     uniforms = (np.float32(1.0) - rs["uniforms"].random((n, gamma + 1), dtype=np.float32)).astype(np.float32)
     return {"hidden_bits": hidden, "W_bits": W, "draft": draft, "q": q, "uniforms": uniforms}
+
+
+# ---------------------------------------------------------------------------
+# Sparse q and the clustered drafter head (inputs only).
+# ---------------------------------------------------------------------------
+def to_sparse_q(q: np.ndarray, *, pad: int = 0, dup: int = 0,
+                shuffle_seed: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(ids, values) form of dense q rows [B, gamma, V] -> two [B, gamma, K] arrays.
+
+    Every nonzero entry of a row is listed; ``dup`` entries per row repeat an
+    id with half its value (the ABI keeps the larger value of a repeated id,
+    so the row still means the same q); ``pad`` padding entries (id -1) fill
+    every row to the same K.  With ``shuffle_seed`` each row's entries are put
+    in a random order.  Pure data movement: no arithmetic on q besides the
+    halving of the repeats.
+    """
+    B, g, V = q.shape
+    nnz = (q != 0).sum(axis=-1)
+    K = int(nnz.max()) + dup + pad
+    ids = np.full((B, g, K), -1, dtype=np.int32)
+    vals = np.zeros((B, g, K), dtype=np.float32)
+    rng = np.random.default_rng(shuffle_seed) if shuffle_seed is not None else None
+    for b in range(B):
+        for i in range(g):
+            nz = np.flatnonzero(q[b, i]).astype(np.int32)
+            v = q[b, i, nz]
+            if dup:
+                pick = nz[:dup] if rng is None else rng.choice(nz, size=min(dup, nz.size), replace=False)
+                nz = np.concatenate([nz, pick])
+                v = np.concatenate([v, (q[b, i, pick] * np.float32(0.5)).astype(np.float32)])
+            n = nz.size
+            ids[b, i, :n] = nz
+            vals[b, i, :n] = v
+            if rng is not None:
+                perm = rng.permutation(K)
+                ids[b, i] = ids[b, i, perm]
+                vals[b, i] = vals[b, i, perm]
+    return ids, vals
+
+
+def truncate_q(x: Dict[str, np.ndarray], K: int, seed: int) -> Dict[str, np.ndarray]:
+    """Inputs whose q rows keep only their K largest entries (renormalised),
+    with the drafts drawn again from the truncated rows (Gumbel-max)."""
+    rs = streams(seed)
+    q = x["q"].astype(np.float64)
+    B, g, V = q.shape
+    out = np.zeros_like(x["q"])
+    draft = np.empty((B, g), dtype=np.int32)
+    for b in range(B):
+        for i in range(g):
+            keep = np.argsort(-q[b, i], kind="stable")[:K]
+            row = np.zeros(V)
+            row[keep] = q[b, i, keep] / q[b, i, keep].sum()
+            out[b, i] = row.astype(np.float32)
+            draft[b, i] = _gumbel_draw(rs["drafts"], out[b, i])
+    y = dict(x)
+    y["q"] = out
+    y["draft"] = draft
+    return y
+
+
+def clustered_head(N: int, d: int, V: int, C: int, M: int, *, w_std: float = 0.02,
+                   seed: int = 0, W_bits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the drafter's clustered head: N hidden rows, W [V, d], a
+    members table [C, M] of disjoint clusters (the first C * M ids of a seeded
+    random permutation of the vocabulary) and the cluster embeddings, each
+    the mean of its members' rows (fp32) rounded to bf16."""
+    rs = streams(seed)
+    cfg = Config("clustered_head", 1, 1, d, V, w_std, 1.0, 0.0, seed=seed)
+    if W_bits is None:
+        W_bits = make_weights(cfg, rs)
+    h = f32_to_bf16_bits(rs["hidden"].standard_normal((N, d), dtype=np.float32))
+    assert C * M <= V, "clusters are disjoint: C * M tokens at most"
+    members = rs["clusters"].permutation(V)[:C * M].reshape(C, M).astype(np.int32)
+    cent = np.empty((C, d), dtype=np.float32)
+    for c in range(C):
+        cent[c] = bf16_bits_to_f32(W_bits[members[c]]).mean(axis=0)
+    return {"h_bits": h, "W_bits": W_bits, "centroid_bits": f32_to_bf16_bits(cent),
+            "members": members}
+
+
+def drafter_chain(B: int, gamma: int, d: int, V: int, C: int, M: int, k: int, *,
+                  w_std: float = 0.02, sigma_h: float = 0.5, seed: int = 0,
+                  W_bits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Inputs of a drafter-then-verifier step with the clustered head.
+
+    The target's hidden rows [B, gamma+1, d]; the drafter's hidden rows at the
+    gamma drafted positions are the target's plus N(0, sigma_h^2) noise
+    (rounded to bf16), [B*gamma, d].  Drafts are drawn (Gumbel-max) from an
+    fp32 approximation of the drafter's sparse q -- top-k clusters by fp32
+    scores, fp32 token logits -- which only shapes the input.
+    """
+    base = clustered_head(B * gamma, d, V, C, M, w_std=w_std, seed=seed, W_bits=W_bits)
+    rs = streams(seed + 1)
+    hidden = f32_to_bf16_bits(rs["hidden"].standard_normal((B, gamma + 1, d), dtype=np.float32))
+    hf = bf16_bits_to_f32(hidden[:, :gamma].reshape(-1, d))
+    hd = f32_to_bf16_bits(hf + rs["noise"].standard_normal(hf.shape, dtype=np.float32)
+                          * np.float32(sigma_h))
+    cent = bf16_bits_to_f32(base["centroid_bits"])
+    hdf = bf16_bits_to_f32(hd)
+    draft = np.empty((B, gamma), dtype=np.int32)
+    for r in range(B * gamma):
+        chosen = np.argsort(-(cent @ hdf[r]), kind="stable")[:k]
+        sel = base["members"][chosen].ravel()
+        sel = sel[(sel >= 0) & (sel < V)]
+        lg = bf16_bits_to_f32(base["W_bits"][sel]) @ hdf[r]
+        qa = np.zeros(V, dtype=np.float32)
+        qa[sel] = _softmax_f64(lg).astype(np.float32)
+        draft[r // gamma, r % gamma] = _gumbel_draw(rs["drafts"], qa)
+    uniforms = (np.float32(1.0) - rs["uniforms"].random((B, gamma + 1), dtype=np.float32)).astype(np.float32)
+    return {"hidden_bits": hidden, "W_bits": base["W_bits"], "h_draft_bits": hd,
+            "centroid_bits": base["centroid_bits"], "members": base["members"], "draft": draft,
+            "uniforms": uniforms}

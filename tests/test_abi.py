@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for name in _declared():
         assert hasattr(raw, name), name
-    assert lib.sv_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.sv_abi_version() == _lib.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -82,6 +82,8 @@ def test_invalid_dims(dims):
     assert lib.sv_accept_and_draw(p, p, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     assert lib.spec_verify_greedy(p, p, p, d, p, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     assert lib.sv_accept_greedy(p, d, p, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
+    assert lib.spec_verify_sparse_q(p, p, p, p, p, 16, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
+    assert lib.sv_accept_and_draw_sparse_q(p, p, p, 16, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     out = ctypes.c_void_p()
     assert lib.sv_debug_views(p, d, ctypes.byref(out), None, None, None) == _lib.SV_ERR_DIMS
 
@@ -153,3 +155,70 @@ def test_debug_views_is_pointer_arithmetic():
     assert all(x % 256 == 0 for x in (logits, rmax, rsum, status))
     assert status + B * 4 <= FAKE + _lib.workspace_bytes(dims)
     assert lib.sv_debug_views(None, dims, None, None, None, None) == _lib.SV_ERR_NULL
+
+
+@no_device
+def test_sparse_q_argument_errors_return_before_launch():
+    lib = _lib.library()
+    d = _lib.Dims(2, 3, 64, 1000)
+    n = _lib.workspace_bytes(d)
+    p = ctypes.c_void_p(FAKE)
+    z = ctypes.c_void_p(0)
+    for K in (0, -1, (1 << 24) + 1):
+        assert lib.spec_verify_sparse_q(p, p, p, p, p, K, p, d, p, p, p, n, None) == _lib.SV_ERR_DIMS
+        assert lib.sv_accept_and_draw_sparse_q(p, p, p, K, p, d, p, p, p, n, None) == _lib.SV_ERR_DIMS
+    # hidden, W, draft, q_ids, q_vals, uniforms, out, n_accepted, workspace NULL in turn
+    for k in range(9):
+        a = [p] * 9
+        a[k] = z
+        assert lib.spec_verify_sparse_q(*a[:5], 16, a[5], d, *a[6:9], n, None) == _lib.SV_ERR_NULL, k
+    # q_ids and q_vals must be 16-byte aligned
+    q4 = ctypes.c_void_p(FAKE + 4)
+    assert lib.spec_verify_sparse_q(p, p, p, q4, p, 16, p, d, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_sparse_q(p, p, p, p, q4, 16, p, d, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_accept_and_draw_sparse_q(p, q4, p, 16, p, d, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_sparse_q(p, p, p, p, p, 16, p, d, p, p, p, n - 1, None) == \
+        _lib.SV_ERR_WORKSPACE
+    assert lib.sv_accept_and_draw_sparse_q(p, p, p, 16, p, d, p, p, p, n - 1, None) == \
+        _lib.SV_ERR_WORKSPACE
+
+
+def _hws(*a):
+    return _lib.sparse_head_workspace_bytes(_lib.HeadDims(*a))
+
+
+def test_sparse_head_workspace_bytes():
+    # N, d, V, C, M, k
+    n = _hws(8, 1536, 262144, 2048, 128, 32)
+    assert n >= 8 * 2048 * 4 + 8 * 4096 * 4 and n % 256 == 0
+    assert _hws(16, 1536, 262144, 2048, 128, 32) > n
+    assert _hws(8, 1536, 262144, 2048, 128, 16) < n
+    for bad in [(0, 16, 64, 8, 8, 2), (65536, 16, 64, 8, 8, 2), (1, 12, 64, 8, 8, 2),
+                (1, 16, 0, 8, 8, 2), (1, 16, 64, 0, 8, 1), (1, 16, 64, 8193, 8, 2),
+                (1, 16, 64, 8, 0, 2), (1, 16, 64, 8, 8, 0), (1, 16, 64, 8, 8, 9),
+                (1, 16, 64, 8192, 4096, 4097)]:
+        assert _hws(*bad) == 0, bad
+
+
+@no_device
+def test_sparse_head_argument_errors_return_before_launch():
+    lib = _lib.library()
+    d = _lib.HeadDims(8, 64, 1000, 50, 20, 4)
+    n = _lib.sparse_head_workspace_bytes(d)
+    p = ctypes.c_void_p(FAKE)
+    z = ctypes.c_void_p(0)
+    odd = ctypes.c_void_p(FAKE + 2)
+    bad = _lib.HeadDims(8, 64, 1000, 50, 20, 51)
+    assert lib.sv_sparse_head(p, p, p, p, bad, p, p, p, p, n, None) == _lib.SV_ERR_DIMS
+    # h, W, centroids, members, q_ids, q_vals NULL in turn, and the workspace
+    for k in (0, 1, 2, 3, 4, 5, 7):
+        a = [p] * 8
+        a[k] = z
+        assert lib.sv_sparse_head(*a[:4], d, *a[4:8], n, None) == _lib.SV_ERR_NULL, k
+    assert lib.sv_sparse_head(odd, p, p, p, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_sparse_head(p, odd, p, p, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_sparse_head(p, p, odd, p, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_sparse_head(p, p, p, odd, d, p, p, p, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_sparse_head(p, p, p, p, d, p, p, p, ctypes.c_void_p(FAKE + 16), n, None) == \
+        _lib.SV_ERR_ALIGN
+    assert lib.sv_sparse_head(p, p, p, p, d, p, p, p, p, n - 1, None) == _lib.SV_ERR_WORKSPACE

@@ -1,0 +1,270 @@
+"""Sparse q and the drafter's clustered head: HIP path vs the fp64 oracle,
+through the C ABI, on an MI355X.
+
+  * spec_verify_sparse_q on (ids, values) rows must give what the oracle's
+    verification gives on the dense rows (same bar as the dense path), and
+    exactly what the HIP dense path gives on those dense rows;
+  * sv_sparse_head must choose the oracle's clusters (except on rows the
+    oracle flags as a near-tie at the k-th cluster, where the choice must be
+    admissible), list their members in cluster order, and give q within
+    1e-5 absolute / 1e-4 relative of the oracle's;
+  * the chain -- sparse head, then sparse verification, device to device --
+    against the oracle's chain.
+
+Every case prints its name, seed and shape before touching the GPU.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import sparse_ref as S
+from oracle import verify_ref as R
+from synth import inputs as I
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+Q_ATOL = 1e-5
+Q_RTOL = 1e-4
+
+
+def _dev():
+    import torch
+    assert torch.cuda.is_available(), "no ROCm device"
+    import draft_token_verification_02_amd as sv
+    sv.library()
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu_sparse(x: dict, ids: np.ndarray, vals: np.ndarray, dev, *, split=False):
+    import torch
+    import draft_token_verification_02_amd as sv
+    t = parity.to_device({"hidden_bits": x["hidden_bits"], "W_bits": x["W_bits"],
+                          "draft": x["draft"], "uniforms": x["uniforms"], "ids": ids,
+                          "vals": vals}, dev)
+    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    ws = sv.new_workspace(dims, dev)
+    if split:
+        out = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+        n = torch.empty((dims.B,), dtype=torch.int32, device=dev)
+        sv.lmhead(t["hidden_bits"], t["W_bits"], ws)
+        sv.accept_and_draw_sparse_q(dims, t["draft"], t["ids"], t["vals"], t["uniforms"], out, n, ws)
+    else:
+        out, n = sv.verify_sparse_q(t["hidden_bits"], t["W_bits"], t["draft"], t["ids"], t["vals"],
+                                    t["uniforms"], workspace=ws)
+    torch.cuda.synchronize()
+    v = sv.debug_views(ws, dims)
+    res = {"out": out.cpu().numpy(), "n": n.cpu().numpy(),
+           "logits": v["logits"].cpu().numpy(), "row_max": v["row_max"].cpu().numpy(),
+           "row_sumexp": v["row_sumexp"].cpu().numpy(), "status": v["status"].cpu().numpy()}
+    del ws, t
+    return res
+
+
+SMALL = [  # (B, gamma, d, V, keep, seed): V ragged / several 4096-chunks, K % 4 != 0, split form
+    (3, 4, 200, 1000, 37, 1),
+    (2, 3, 256, 9000, 400, 2),
+    (1, 4, 64, 33, 5, 3),
+    (20, 4, 64, 4500, 64, 4),       # 40 draw workgroups: fused form
+    (40, 2, 32, 5000, 129, 5),      # 80 draw workgroups: split form
+    (2, 8, 1536, 12288, 2048, 6),
+]
+
+
+@pytest.mark.parametrize("B,gamma,d,V,keep,seed", SMALL)
+def test_sparse_q_small_parity(B, gamma, d, V, keep, seed):
+    dev = _dev()
+    _say(f"sparse-q small B={B} gamma={gamma} d={d} V={V} keep={keep} seed={seed}")
+    x = I.truncate_q(I.custom(B, gamma, d, V, seed=seed, sigma=0.8), keep, seed + 100)
+    ids, vals = I.to_sparse_q(x["q"], pad=3, dup=2, shuffle_seed=seed)
+    rep = parity.compare(x, run_gpu_sparse(x, ids, vals, dev))
+    _say("sparse-q small", rep)
+
+
+def test_sparse_q_equals_dense_path_bitwise():
+    dev = _dev()
+    _say("sparse-q vs dense bitwise B=6 gamma=4 d=128 V=6000 seed=7 (both forms)")
+    x = I.truncate_q(I.custom(6, 4, 128, 6000, seed=7, sigma=0.8), 300, 107)
+    ids, vals = I.to_sparse_q(x["q"], shuffle_seed=7)
+    dense = parity.run_gpu(x, dev)
+    for split in (False, True):
+        sp = run_gpu_sparse(x, ids, vals, dev, split=split)
+        for k in ("out", "n", "logits", "row_max", "row_sumexp", "status"):
+            np.testing.assert_array_equal(sp[k], dense[k], err_msg=k)
+    # many sequences: the split (accept / draw / pick) form
+    x = I.truncate_q(I.custom(30, 4, 64, 9000, seed=8, sigma=0.8), 100, 108)
+    ids, vals = I.to_sparse_q(x["q"], pad=1, shuffle_seed=8)
+    dense = parity.run_gpu(x, dev)
+    sp = run_gpu_sparse(x, ids, vals, dev)
+    for k in ("out", "n", "status"):
+        np.testing.assert_array_equal(sp[k], dense[k], err_msg=k)
+
+
+def test_sparse_q_ids_out_of_range_are_ignored_and_flagged():
+    dev = _dev()
+    _say("sparse-q bad ids B=3 gamma=3 d=64 V=700 seed=9")
+    x = I.truncate_q(I.custom(3, 3, 64, 700, seed=9, sigma=0.8), 40, 109)
+    ids, vals = I.to_sparse_q(x["q"], pad=2)
+    ids[1, 0, -1] = 700            # >= V: ignored, flags sequence 1
+    vals[1, 0, -1] = 0.5
+    ids[2, 2, -2] = 10 ** 6
+    vals[2, 2, -2] = 0.25
+    gpu = run_gpu_sparse(x, ids, vals, dev)
+    parity.compare(x, gpu)
+    assert gpu["status"][0] & 8 == 0
+    assert gpu["status"][1] & 8 and gpu["status"][2] & 8
+
+
+def test_sparse_q_full_config_parity():
+    dev = _dev()
+    cfg = I.CONFIGS["sparse_q"]
+    _say(f"sparse-q full B={cfg.B} gamma={cfg.gamma} d={cfg.d} V={cfg.V} seed={cfg.seed}")
+    x = I.generate(cfg)
+    ids, vals = I.to_sparse_q(x["q"], shuffle_seed=3)
+    assert ids.shape[-1] == 32 * 128
+    rep = parity.compare(x, run_gpu_sparse(x, ids, vals, dev))
+    _say("sparse-q full", rep)
+
+
+# ---------------------------------------------------------------------------
+def run_gpu_head(x: dict, k: int, dev):
+    import torch
+    import draft_token_verification_02_amd as sv
+    t = parity.to_device({"h": x["h_bits"], "W": x["W_bits"], "cent": x["centroid_bits"],
+                          "members": x["members"]}, dev)
+    ids, vals, cl = sv.sparse_head(t["h"], t["W"], t["cent"], t["members"], k)
+    torch.cuda.synchronize()
+    res = {"ids": ids.cpu().numpy(), "vals": vals.cpu().numpy(), "clusters": cl.cpu().numpy()}
+    del t
+    return res
+
+
+def compare_head(x: dict, k: int, gpu: dict) -> dict:
+    V = x["W_bits"].shape[0]
+    ref = S.sparse_head(x["h_bits"], x["W_bits"], x["centroid_bits"], x["members"], k)
+    N = x["h_bits"].shape[0]
+    rep = {"rows": N, "flagged": int(ref.flagged.sum()), "flagged_differ": 0,
+           "max_abs_dq": 0.0, "max_rel_dq": 0.0}
+    for n in range(N):
+        cl = gpu["clusters"][n]
+        assert np.all(np.diff(cl) > 0), f"row {n}: clusters not ascending"
+        if not ref.flagged[n]:
+            assert np.array_equal(cl, ref.clusters[n]), f"row {n}: clusters differ"
+        else:
+            s = ref.scores[n]
+            other = np.setdiff1d(np.arange(s.shape[0]), cl)
+            assert s[cl].min() >= (s[other].max() if other.size else -np.inf) - S.TOPK_BAND, n
+            if not np.array_equal(cl, ref.clusters[n]):
+                rep["flagged_differ"] += 1
+                continue
+        # ids: the chosen clusters' members in cluster order, dropped ids as -1
+        want = x["members"][cl].ravel()
+        want = np.where((want >= 0) & (want < V), want, -1)
+        assert np.array_equal(gpu["ids"][n], want), f"row {n}: ids"
+        # values, matched by id against the oracle's ascending list
+        live = want >= 0
+        order = np.argsort(want[live], kind="stable")
+        got = gpu["vals"][n][live][order].astype(np.float64)
+        assert np.array_equal(want[live][order], ref.idx[n])
+        dq = np.abs(got - ref.val[n])
+        assert dq.max() <= Q_ATOL, f"row {n}: max |dq| {dq.max()}"
+        rel = (dq / ref.val[n]).max()
+        assert rel <= Q_RTOL, f"row {n}: max rel dq {rel}"
+        assert np.all(gpu["vals"][n][~live] == 0)
+        rep["max_abs_dq"] = max(rep["max_abs_dq"], float(dq.max()))
+        rep["max_rel_dq"] = max(rep["max_rel_dq"], float(rel))
+    return rep
+
+
+HEAD_SMALL = [  # (N, d, V, C, M, k, seed)
+    (4, 64, 1024, 64, 16, 4, 1),
+    (17, 200, 3000, 90, 30, 7, 2),       # C*M < V: part of the vocabulary in no cluster
+    (40, 1536, 8192, 512, 16, 32, 3),    # N > 32: three hidden-row fragments
+    (3, 32, 500, 300, 1, 300, 4),        # every cluster chosen
+    (70, 8, 64, 8, 8, 1, 5),             # N > 64, tiny d
+]
+
+
+@pytest.mark.parametrize("N,d,V,C,M,k,seed", HEAD_SMALL)
+def test_sparse_head_small_parity(N, d, V, C, M, k, seed):
+    dev = _dev()
+    _say(f"sparse head N={N} d={d} V={V} C={C} M={M} k={k} seed={seed}")
+    x = I.clustered_head(N, d, V, C, M, w_std=0.3, seed=seed)
+    rep = compare_head(x, k, run_gpu_head(x, k, dev))
+    _say("sparse head", rep)
+
+
+def test_sparse_head_drops_out_of_range_members():
+    dev = _dev()
+    _say("sparse head bad members N=5 d=64 V=1000 C=40 M=25 k=40 seed=6")
+    x = I.clustered_head(5, 64, 1000, 40, 25, w_std=0.3, seed=6)
+    x["members"][3, 4] = -7
+    x["members"][10, 0] = 1000
+    gpu = run_gpu_head(x, 40, dev)
+    for n in range(5):
+        assert np.count_nonzero(gpu["ids"][n] == -1) == 2
+        assert abs(gpu["vals"][n].astype(np.float64).sum() - 1.0) < 1e-5
+    # against the oracle on the table without the dropped entries: all clusters chosen
+    flat = x["members"].ravel()
+    keep = flat[(flat >= 0) & (flat < 1000)]
+    for n in range(5):
+        ref = S.sparse_head(x["h_bits"][n:n + 1], x["W_bits"], x["W_bits"][:1], keep[None, :], 1)
+        live = gpu["ids"][n] >= 0
+        order = np.argsort(gpu["ids"][n][live], kind="stable")
+        np.testing.assert_allclose(gpu["vals"][n][live][order], ref.val[0], rtol=Q_RTOL, atol=Q_ATOL)
+
+
+def test_sparse_head_full_shape_parity():
+    dev = _dev()
+    N, d, V, C, M, k = 32, 1536, 262144, 2048, 128, 32
+    _say(f"sparse head full N={N} d={d} V={V} C={C} M={M} k={k} seed=0")
+    x = I.clustered_head(N, d, V, C, M, seed=0)
+    rep = compare_head(x, k, run_gpu_head(x, k, dev))
+    _say("sparse head full", rep)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,gamma,d,V,C,M,k,seed", [
+    (3, 4, 128, 4096, 128, 32, 8, 1),
+    (8, 4, 1536, 262144, 2048, 128, 32, 0),
+])
+def test_drafter_then_verifier_chain(B, gamma, d, V, C, M, k, seed):
+    import torch
+    import draft_token_verification_02_amd as sv
+    dev = _dev()
+    _say(f"chain B={B} gamma={gamma} d={d} V={V} C={C} M={M} k={k} seed={seed}")
+    x = I.drafter_chain(B, gamma, d, V, C, M, k, seed=seed)
+    t = parity.to_device(x, dev)
+    ids, vals, cl = sv.sparse_head(t["h_draft_bits"], t["W_bits"], t["centroid_bits"], t["members"], k)
+    K = k * M
+    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    ws = sv.new_workspace(dims, dev)
+    out, n = sv.verify_sparse_q(t["hidden_bits"], t["W_bits"], t["draft"],
+                                ids.view(B, gamma, K), vals.view(B, gamma, K), t["uniforms"],
+                                workspace=ws)
+    torch.cuda.synchronize()
+    v = sv.debug_views(ws, dims)
+    gpu = {"out": out.cpu().numpy(), "n": n.cpu().numpy(), "logits": v["logits"].cpu().numpy(),
+           "row_max": v["row_max"].cpu().numpy(), "row_sumexp": v["row_sumexp"].cpu().numpy()}
+    # the oracle's chain: its own sparse head, densified, then its verification
+    head = S.sparse_head(x["h_draft_bits"], x["W_bits"], x["centroid_bits"], x["members"], k)
+    q = S.densify(head.idx.reshape(B, gamma, K), head.val.reshape(B, gamma, K), V)
+    xo = {"hidden_bits": x["hidden_bits"], "W_bits": x["W_bits"], "draft": x["draft"],
+          "q": q.astype(np.float32), "uniforms": x["uniforms"]}
+    # A drafted row the oracle flags as a near-tie at the k-th cluster may choose
+    # other clusters on the GPU (checked admissible by the head tests); its
+    # sequence is then compared only if both sides chose the same clusters.
+    same = np.all(cl.cpu().numpy().reshape(B, gamma, k) == head.clusters.reshape(B, gamma, k),
+                  axis=(1, 2))
+    ok = ~head.flagged.reshape(B, gamma).any(axis=1) | same
+    assert ok.sum() >= B - 1, "more than one sequence lost to near-ties"
+    rep = parity.compare(xo, gpu, seqs=np.flatnonzero(ok))
+    rep["flagged_rows"] = int(head.flagged.sum())
+    _say("chain", rep)

@@ -76,3 +76,46 @@ def test_config_registry_shapes():
     assert (c["gemma_e2b"].V, c["gemma_e2b"].d, c["gemma_e2b"].R) == (262144, 1536, 5)
     assert c["llama8b_g8_b4"].R == 36 and c["sweep_b256_s1.0"].R == 1280
     assert c["sparse_q"].sparse == (2048, 128, 32) and c["sparse_q"].R == 40
+
+
+def test_to_sparse_q_lists_every_nonzero_once_with_repeats_and_padding():
+    x = I.truncate_q(I.custom(2, 3, 32, 300, seed=3), 20, 4)
+    ids, vals = I.to_sparse_q(x["q"], pad=3, dup=2, shuffle_seed=1)
+    assert ids.shape == vals.shape == (2, 3, 20 + 2 + 3)
+    assert ids.dtype == np.int32 and vals.dtype == np.float32
+    for b in range(2):
+        for i in range(3):
+            live = ids[b, i] >= 0
+            assert np.count_nonzero(~live) == 3 and np.all(vals[b, i, ~live] == 0)
+            dense = np.zeros(300, dtype=np.float32)
+            np.maximum.at(dense, ids[b, i, live], vals[b, i, live])   # a repeated id keeps its larger value
+            np.testing.assert_array_equal(dense, x["q"][b, i])
+            assert np.unique(ids[b, i, live]).size == 20
+
+
+def test_truncate_q_keeps_k_entries_and_draws_from_them():
+    x = I.custom(3, 4, 32, 500, seed=5)
+    y = I.truncate_q(x, 17, 6)
+    assert np.all((y["q"] != 0).sum(-1) == 17)
+    np.testing.assert_allclose(y["q"].sum(-1), 1.0, atol=1e-6)
+    for b in range(3):
+        for i in range(4):
+            assert y["q"][b, i, y["draft"][b, i]] > 0
+            top = np.argsort(-x["q"][b, i], kind="stable")[:17]
+            assert set(np.flatnonzero(y["q"][b, i])) == set(top)
+
+
+def test_clustered_head_inputs():
+    x = I.clustered_head(5, 24, 1000, 30, 20, w_std=0.3, seed=2)
+    m = x["members"]
+    assert m.shape == (30, 20) and m.dtype == np.int32
+    assert np.unique(m).size == m.size and m.min() >= 0 and m.max() < 1000
+    cent = I.bf16_bits_to_f32(x["centroid_bits"])
+    W = I.bf16_bits_to_f32(x["W_bits"])
+    for c in (0, 17, 29):
+        np.testing.assert_allclose(cent[c], W[m[c]].mean(axis=0), rtol=1e-2, atol=1e-3)
+    y = I.drafter_chain(2, 3, 24, 1024, 32, 32, 4, seed=3)
+    assert y["h_draft_bits"].shape == (6, 24) and y["hidden_bits"].shape == (2, 4, 24)
+    for r in range(6):
+        # drafts are members of some cluster
+        assert np.isin(y["draft"][r // 3, r % 3], y["members"])
