@@ -21,7 +21,7 @@ ABI_VERSION = 3
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
            "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views",
            "spec_verify_sparse_q", "sv_accept_and_draw_sparse_q", "sv_sparse_head_workspace_bytes",
-           "sv_sparse_head")
+           "sv_sparse_head", "sv_tree_shape", "sv_tree_workspace_bytes", "spec_verify_tree")
 
 
 class Dims(ctypes.Structure):
@@ -76,6 +76,12 @@ def _load():
         lib.sv_sparse_head_workspace_bytes.argtypes = [HeadDims]
         lib.sv_sparse_head.restype = st
         lib.sv_sparse_head.argtypes = [vp, vp, vp, vp, HeadDims, vp, vp, vp, vp, sz, vp]
+        lib.sv_tree_shape.restype = st
+        lib.sv_tree_shape.argtypes = [vp, ctypes.c_int32, vp, vp, vp]
+        lib.sv_tree_workspace_bytes.restype = sz
+        lib.sv_tree_workspace_bytes.argtypes = [Dims]
+        lib.spec_verify_tree.restype = st
+        lib.spec_verify_tree.argtypes = [vp, vp, vp, vp, vp, vp, Dims, vp, vp, vp, vp, sz, vp]
         lib.sv_debug_views.restype = st
         lib.sv_debug_views.argtypes = [vp, Dims, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), ctypes.POINTER(vp)]
@@ -321,6 +327,69 @@ def sparse_head(h, W, centroids, members, k: int, *, q_ids=None, q_vals=None, cl
     if st != SV_OK:
         raise SVError(st, "sv_sparse_head")
     return q_ids, q_vals, clusters
+
+
+def _host_parent(parent):
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    if arr.ndim != 1:
+        raise ValueError("parent must be a 1-d list of node parents")
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def tree_shape(parent):
+    """(depth D, q rows P, launch rounds) of a topology; raises SVError if invalid."""
+    arr, ptr = _host_parent(parent)
+    out = [ctypes.c_int32() for _ in range(3)]
+    st = _load().sv_tree_shape(ptr, int(arr.size), *[ctypes.byref(o) for o in out])
+    if st != SV_OK:
+        raise SVError(st, "sv_tree_shape")
+    return tuple(int(o.value) for o in out)
+
+
+def tree_workspace_bytes(dims: Dims) -> int:
+    return int(_load().sv_tree_workspace_bytes(dims))
+
+
+def verify_tree(hidden, W, parent, tokens, q, uniforms, *, out_tokens=None, n_accepted=None,
+                path_nodes=None, workspace=None, stream=None):
+    """Tree verification; returns (out_tokens [B, D+1], n_accepted [B], path_nodes [B, D]).
+
+    hidden bf16 [B, T+1, d]; W bf16 [V, d]; parent host ints [T]; tokens int32
+    [B, T]; q float32 [B, P, V] (rows with children); uniforms float32 [B, T+1].
+    """
+    import torch
+    arr, pptr = _host_parent(parent)
+    D, P, _ = tree_shape(arr)
+    _check_inputs(hidden, W, None, None, uniforms)
+    B, T1, d = hidden.shape
+    V = W.shape[0]
+    if T1 - 1 != arr.size:
+        raise ValueError(f"hidden has {T1} rows per sequence, the tree {arr.size} nodes + root")
+    if tokens.dtype != torch.int32 or tuple(tokens.shape) != (B, T1 - 1) or not tokens.is_contiguous():
+        raise ValueError(f"tokens must be contiguous int32 [{B}, {T1 - 1}]")
+    if q.dtype != torch.float32 or tuple(q.shape) != (B, P, V) or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous float32 [{B}, {P}, {V}]")
+    dims = Dims(B, T1 - 1, d, V)
+    dev = W.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if path_nodes is None:
+        path_nodes = torch.empty((B, D), dtype=torch.int32, device=dev)
+    if workspace is None:
+        n = tree_workspace_bytes(dims)
+        if n == 0:
+            raise SVError(SV_ERR_DIMS, "sv_tree_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = _load().spec_verify_tree(_ptr(hidden), _ptr(W), pptr, _ptr(tokens), _ptr(q),
+                                  _ptr(uniforms), dims, _ptr(out_tokens), _ptr(n_accepted),
+                                  _ptr(path_nodes), _ptr(workspace), workspace.numel(),
+                                  _stream_handle(dev, stream))
+    if st != SV_OK:
+        raise SVError(st, "spec_verify_tree")
+    return out_tokens, n_accepted, path_nodes
 
 
 def debug_views(workspace, dims: Dims) -> dict:

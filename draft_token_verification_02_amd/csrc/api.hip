@@ -2,6 +2,8 @@
 // argument validation, workspace carving and kernel launches on the
 // caller's stream.  No allocation, no synchronisation, no state.
 
+#include <algorithm>
+
 #include "sv_common.h"
 
 namespace sv {
@@ -26,6 +28,12 @@ hipError_t launch_sparse_head(const uint16_t* h, const uint16_t* W, const uint16
                               const int32_t* members, int N, int d, int V, int C, int M, int k,
                               int32_t* q_ids, float* q_vals, int32_t* clusters, void* ws,
                               hipStream_t stream);
+hipError_t launch_tree(const float* logits, const float* part_max, const float* part_sum, int NP,
+                       int NPs, int B, int V, const TreeTopo& tp, int rounds,
+                       const int32_t* tokens, const float* q, const float* uniforms, int NC,
+                       double* csum, double* psum, float* row_max, float* row_sum, void* state,
+                       int32_t* out_tokens, int32_t* n_accepted, int32_t* path_nodes,
+                       int32_t* status, hipStream_t stream);
 }  // namespace sv
 
 namespace {
@@ -134,6 +142,52 @@ bool head_dims_ok(sv_head_dims d) {
     return d.N >= 1 && d.N <= 65535 && d.d >= 8 && d.d <= 65536 && d.d % 8 == 0 && d.V >= 1 &&
            d.V <= (1 << 28) && d.C >= 1 && d.C <= SV_HEAD_MAX_CLUSTERS && d.M >= 1 && d.k >= 1 &&
            d.k <= d.C && (int64_t)d.k * d.M <= (1 << 24);
+}
+
+bool tree_dims_ok(sv_dims d) {
+    if (!(d.B >= 1 && d.B <= (1 << 20) && d.gamma >= 1 && d.gamma <= SV_MAX_TREE_NODES &&
+          d.d >= 8 && d.d <= 65536 && d.d % 8 == 0 && d.V >= 1 && d.V <= (1 << 28)))
+        return false;
+    const int64_t chunks = (d.V + sv::kDrawChunk - 1) / sv::kDrawChunk;
+    return (int64_t)d.B * chunks <= INT32_MAX;
+}
+
+// The most residual sums one walk from node v can need, plus its draw: a
+// first child is tested against p; each rejection before the last child
+// needs a sum to test the next one; the draw needs one.
+int tree_rounds(const sv::TreeTopo& tp, int v) {
+    const int row = v + 1;
+    int t = tp.first_child[row];
+    if (t < 0) return 1;
+    int best = 0, j = 0;
+    for (; t >= 0; t = tp.next_sibling[t], ++j) best = std::max(best, j + tree_rounds(tp, t));
+    return std::max(best, j);                   // j children, all rejected
+}
+
+// Validates parent[] and builds the kernels' view of the topology.
+bool build_topology(const int32_t* parent, int T, sv::TreeTopo* tp, int* rounds) {
+    if (!parent || T < 1 || T > SV_MAX_TREE_NODES) return false;
+    tp->T = T;
+    for (int r = 0; r <= T; ++r) { tp->first_child[r] = -1; tp->qslot[r] = -1; }
+    int depth[SV_MAX_TREE_NODES];
+    int last_child[SV_MAX_TREE_NODES + 1];
+    for (int r = 0; r <= T; ++r) last_child[r] = -1;
+    tp->D = 0;
+    for (int t = 0; t < T; ++t) {
+        const int a = parent[t];
+        if (a < -1 || a >= t) return false;
+        depth[t] = a < 0 ? 1 : depth[a] + 1;
+        tp->D = std::max(tp->D, depth[t]);
+        tp->next_sibling[t] = -1;
+        if (last_child[a + 1] < 0) tp->first_child[a + 1] = (int8_t)t;
+        else tp->next_sibling[last_child[a + 1]] = (int8_t)t;
+        last_child[a + 1] = t;
+    }
+    tp->P = 0;
+    for (int r = 0; r <= T; ++r)
+        if (tp->first_child[r] >= 0) tp->qslot[r] = (int8_t)tp->P++;
+    if (rounds) *rounds = tree_rounds(*tp, -1);
+    return true;
 }
 
 sv_status check_greedy(const int32_t* draft, sv_dims dims, const int32_t* out_tokens,
@@ -275,6 +329,54 @@ sv_status spec_verify_greedy(const uint16_t* hidden, const uint16_t* W_lmhead,
     st = stage1(hidden, W_lmhead, dims, workspace, s, /*keep_logits=*/false);
     if (st != SV_OK) return st;
     return stage2_greedy(draft_tokens, dims, out_tokens, n_accepted, target_tokens, workspace, s);
+}
+
+sv_status sv_tree_shape(const int32_t* parent, int32_t T, int32_t* depth, int32_t* q_rows,
+                        int32_t* rounds) {
+    sv::TreeTopo tp;
+    int r;
+    if (!build_topology(parent, T, &tp, &r)) return SV_ERR_DIMS;
+    if (depth) *depth = tp.D;
+    if (q_rows) *q_rows = tp.P;
+    if (rounds) *rounds = r;
+    return SV_OK;
+}
+
+size_t sv_tree_workspace_bytes(sv_dims dims) {
+    if (!tree_dims_ok(dims)) return 0;
+    return sv::make_layout(dims.B, dims.gamma, dims.d, dims.V).total;
+}
+
+sv_status spec_verify_tree(const uint16_t* hidden, const uint16_t* W_lmhead, const int32_t* parent,
+                           const int32_t* tree_tokens, const float* q, const float* uniforms,
+                           sv_dims dims, int32_t* out_tokens, int32_t* n_accepted,
+                           int32_t* path_nodes, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    if (!tree_dims_ok(dims)) return SV_ERR_DIMS;
+    sv::TreeTopo tp;
+    int rounds;
+    if (!parent) return SV_ERR_NULL;
+    if (!build_topology(parent, dims.gamma, &tp, &rounds)) return SV_ERR_DIMS;
+    if (!hidden || !W_lmhead || !tree_tokens || !q || !uniforms || !out_tokens || !n_accepted ||
+        !workspace)
+        return SV_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(W_lmhead, 16) || !aligned(q, 16) ||
+        !aligned(tree_tokens, 4) || !aligned(uniforms, 4) || !aligned(out_tokens, 4) ||
+        !aligned(n_accepted, 4) || !aligned(path_nodes, 4) || !aligned(workspace, 256))
+        return SV_ERR_ALIGN;
+    if (workspace_bytes < sv_tree_workspace_bytes(dims)) return SV_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const sv_status st = stage1(hidden, W_lmhead, dims, workspace, s);
+    if (st != SV_OK) return st;
+    const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
+    const hipError_t e = sv::launch_tree(
+        at<float>(workspace, L.logits), at<float>(workspace, L.part_max),
+        at<float>(workspace, L.part_sum), lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.V, tp,
+        rounds, tree_tokens, q, uniforms, L.NC, at<double>(workspace, L.csum),
+        at<double>(workspace, L.psum), at<float>(workspace, L.row_max),
+        at<float>(workspace, L.row_sum), at<char>(workspace, L.tstate), out_tokens, n_accepted,
+        path_nodes, at<int32_t>(workspace, L.status), s);
+    return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
 sv_status sv_debug_views(const void* workspace, sv_dims dims, const float** logits,

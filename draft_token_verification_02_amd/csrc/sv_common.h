@@ -49,8 +49,10 @@ static inline bool lmhead_use_tiled(int R, int V) {
 struct Layout {
     int R, NPs, NC;
     size_t logits, part_max, part_sum, part_arg, row_max, row_sum, status, counters, csum, psum,
-        total;
+        tstate, total;
 };
+
+constexpr size_t kTreeStateBytes = 32;   // per-sequence walk state of tree verification
 
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -74,6 +76,7 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     L.counters = off; off = align_up(off + (size_t)B * sizeof(int32_t), 256);
     L.csum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
     L.psum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
+    L.tstate = off;   off = align_up(off + (size_t)B * kTreeStateBytes, 256);
     L.total = off;
     return L;
 }
@@ -85,6 +88,17 @@ struct HeadLayout {
     size_t scores, tl, pmax, psum, total;
 };
 HeadLayout make_head_layout(int N, int C, int K);
+
+// Static topology of a draft tree, passed to the tree kernels by value.
+// Rows: 0 for the root, t + 1 for node t.
+struct TreeTopo {
+    int T;                                       // nodes
+    int D;                                       // deepest node's depth
+    int P;                                       // rows with children (q rows)
+    int8_t first_child[SV_MAX_TREE_NODES + 1];   // per row: first child node, -1 for none
+    int8_t next_sibling[SV_MAX_TREE_NODES];      // per node: next child of its parent, -1
+    int8_t qslot[SV_MAX_TREE_NODES + 1];         // per row: its q row, -1 without children
+};
 
 // Merge of two (max, sum of exp(x - max)) pairs: the online-softmax step.
 // Symmetric in its two arguments, so a butterfly gives every lane the same bits.

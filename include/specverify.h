@@ -178,6 +178,52 @@ SV_API sv_status sv_accept_and_draw_sparse_q(const int32_t *draft_tokens, const 
                                       void *hip_stream);
 
 /* ------------------------------------------------------------------------
+ * Tree verification: several drafted candidates per position, laid out as a
+ * static tree, all scored by the same single pass over W, and checked with
+ * the rule of spec_verify at every fork ("推测解码", section on later
+ * methods: EAGLE checks its guess tree with the same rule at every fork,
+ * which keeps the distribution; sections 通过的规则 and 留下对的，换掉错的 for
+ * the rule).  At a node, its children are tested in increasing node index:
+ * the first with r * q(x) <= p(x) against p of the node's row, each later
+ * one against the renormalised residual max(0, cur - q) / sum the previous
+ * rejection left.  A kept child is emitted and checking continues at its
+ * row with its own children; when every child is rejected the token is
+ * drawn from the last residual, and at a node without children the bonus
+ * token is drawn from p of its row (inverse CDF over ascending id, u =
+ * uniforms[b][T]).  A path topology (parent[t] = t - 1) is spec_verify.
+ *
+ *   parent       HOST int32 [T]: parent[t] < t, -1 for the root's children
+ *   hidden       bf16 bits [B][T+1][d]: row 0 the root (last context
+ *                position), row t+1 node t
+ *   tree_tokens  int32 [B][T]: the candidate token of every node
+ *   q            fp32 [B][P][V]: the drafter's q at every row that has
+ *                children, in row order (P such rows; sv_tree_shape)
+ *   uniforms     fp32 [B][T+1] in (0,1]: [:, t] node t's test, [:, T] the draw
+ *   dims         B, gamma = T, d, V
+ *   out_tokens   int32 [B][D+1]: the kept tokens root to leaf, the drawn
+ *                token, -1 after (D = depth of the deepest node)
+ *   n_accepted   int32 [B]: kept tokens
+ *   path_nodes   int32 [B][D] or NULL: node index of every kept token, -1 after
+ * The workspace is sv_tree_workspace_bytes(dims).  Work on the stream: the
+ * LM head, then 1 + 2 * rounds launches (rounds from sv_tree_shape). */
+#define SV_MAX_TREE_NODES 64
+
+/* Depth D, q rows P and launch rounds of a topology; SV_ERR_DIMS if parent
+ * is not a valid tree (1 <= T <= SV_MAX_TREE_NODES, -1 <= parent[t] < t).
+ * Host only; any output may be NULL. */
+SV_API sv_status sv_tree_shape(const int32_t *parent, int32_t T, int32_t *depth, int32_t *q_rows,
+                        int32_t *rounds);
+
+/* Workspace bytes of spec_verify_tree (dims.gamma = T); 0 if dims are invalid. */
+SV_API size_t sv_tree_workspace_bytes(sv_dims dims);
+
+SV_API sv_status spec_verify_tree(const uint16_t *hidden, const uint16_t *W_lmhead,
+                           const int32_t *parent, const int32_t *tree_tokens, const float *q,
+                           const float *uniforms, sv_dims dims, int32_t *out_tokens,
+                           int32_t *n_accepted, int32_t *path_nodes, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------
  * The drafter's clustered sparse LM head, which produces that sparse q
  * ("多詞元預測視覺化指南", section 高效嵌入器): the vocabulary is grouped into C
  * clusters of M tokens, each cluster with an embedding of its own.  For each

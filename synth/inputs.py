@@ -407,3 +407,77 @@ def drafter_chain(B: int, gamma: int, d: int, V: int, C: int, M: int, k: int, *,
     return {"hidden_bits": hidden, "W_bits": base["W_bits"], "h_draft_bits": hd,
             "centroid_bits": base["centroid_bits"], "members": base["members"], "draft": draft,
             "uniforms": uniforms}
+
+
+# ---------------------------------------------------------------------------
+# Draft trees (inputs only).
+# ---------------------------------------------------------------------------
+def tree_rows_with_children(parent) -> np.ndarray:
+    """Rows (0 = root, t+1 = node t) that have children, in row order."""
+    has = np.zeros(len(parent) + 1, dtype=bool)
+    for a in parent:
+        has[int(a) + 1] = True
+    return np.flatnonzero(has)
+
+
+def tree_inputs(B: int, parent, d: int, V: int, *, w_std: float = 0.5, sigma: float = 0.7,
+                seed: int = 0, W_bits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Inputs of tree verification with the recipe of ``generate``.
+
+    hidden [B, T+1, d] (row 0 the root, row t+1 node t); q [B, P, V] at the
+    rows with children, softmax of fp32 approximate logits plus N(0, sigma^2);
+    every node's token drawn (Gumbel-max) from q at its parent's row, siblings
+    independently; uniforms [B, T+1] = 1 - U.
+    """
+    T = len(parent)
+    cfg = Config(f"tree_B{B}_T{T}_d{d}_V{V}", B, T, d, V, w_std, 1.0, sigma, seed=seed)
+    rs = streams(seed)
+    if W_bits is None:
+        W_bits = make_weights(cfg, rs)
+    hidden = f32_to_bf16_bits(rs["hidden"].standard_normal((B, T + 1, d), dtype=np.float32))
+    rows = tree_rows_with_children(parent)
+    slot = {int(r): i for i, r in enumerate(rows)}
+    lg = approx_target_logits(hidden[:, rows, :], W_bits).reshape(B, rows.size, V)
+    q = np.empty((B, rows.size, V), dtype=np.float32)
+    for b in range(B):
+        noise = rs["noise"].standard_normal((rows.size, V), dtype=np.float32) * np.float32(sigma)
+        q[b] = _softmax_f64(lg[b] + noise).astype(np.float32)
+    tokens = np.empty((B, T), dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            tokens[b, t] = _gumbel_draw(rs["drafts"], q[b, slot[int(parent[t]) + 1]])
+    uniforms = (np.float32(1.0) - rs["uniforms"].random((B, T + 1), dtype=np.float32)).astype(np.float32)
+    return {"hidden_bits": hidden, "W_bits": W_bits, "parent": np.asarray(parent, dtype=np.int32),
+            "tokens": tokens, "q": q, "uniforms": uniforms}
+
+
+def tree_repeated_trials(base: Dict[str, np.ndarray], n: int, seed: int) -> Dict[str, np.ndarray]:
+    """``n`` trials of sequence 0 of ``base``: hidden states, weights and q
+    shared; every node's token (from q at its parent's row) and the uniforms
+    fresh per trial.  Small V only."""
+    rs = streams(seed)
+    parent = base["parent"]
+    T = len(parent)
+    rows = tree_rows_with_children(parent)
+    slot = {int(r): i for i, r in enumerate(rows)}
+    q = np.repeat(base["q"][:1], n, axis=0)
+    V = q.shape[-1]
+    tokens = np.empty((n, T), dtype=np.int32)
+    with np.errstate(divide="ignore"):
+        for t in range(T):
+            lq = np.log(base["q"][0, slot[int(parent[t]) + 1]].astype(np.float64))
+            u = rs["drafts"].random((n, V))
+            tokens[:, t] = np.argmax(lq[None, :] - np.log(-np.log(u)), axis=-1)
+    uniforms = (np.float32(1.0) - rs["uniforms"].random((n, T + 1), dtype=np.float32)).astype(np.float32)
+    return {"hidden_bits": np.repeat(base["hidden_bits"][:1], n, axis=0), "W_bits": base["W_bits"],
+            "parent": parent, "tokens": tokens, "q": q, "uniforms": uniforms}
+
+
+# A static tree of 25 nodes in the shape EAGLE-style drafters use: wide near
+# the root, narrowing with depth (4 root candidates; their children 3, 2, 1, 1;
+# and so on to depth 5).
+EAGLE_LIKE_TREE = [-1, -1, -1, -1,          # depth 1: nodes 0-3
+                   0, 0, 0, 1, 1, 2, 3,     # depth 2: nodes 4-10
+                   4, 4, 5, 7, 9, 10,       # depth 3: nodes 11-16
+                   11, 11, 13, 14, 16,      # depth 4: nodes 17-21
+                   17, 19, 21]              # depth 5: nodes 22-24

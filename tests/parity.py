@@ -218,3 +218,77 @@ def compare_greedy(x: dict, draft: np.ndarray, gpu: dict, ref, seqs=None) -> dic
         assert gpu["out"][b, n] == (yn if yn >= 0 else 0)
         assert all(v == -1 for v in gpu["out"][b, n + 1:])
     return rep
+
+
+# ---------------------------------------------------------------------------
+# Tree verification.
+#
+# The bar: logits and p as for the chain; the kept path (node indices) equal
+# to the oracle's unless some test on the oracle's walk is flagged as lying
+# within 1e-5 of its boundary -- then the GPU's path must still be a path of
+# the tree carrying the nodes' tokens, and its draw is not compared; with
+# equal paths the drawn token is equal unless the oracle flags the draw, and
+# then admissible.
+# ---------------------------------------------------------------------------
+def run_gpu_tree(x: dict, dev):
+    import torch
+    import draft_token_verification_02_amd as sv
+    t = to_device({k: x[k] for k in ("hidden_bits", "W_bits", "tokens", "q", "uniforms")}, dev)
+    B, T1, d = x["hidden_bits"].shape
+    dims = sv.Dims(B, T1 - 1, d, x["W_bits"].shape[0])
+    ws = torch.empty(sv.tree_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    out, n, path = sv.verify_tree(t["hidden_bits"], t["W_bits"], x["parent"], t["tokens"], t["q"],
+                                  t["uniforms"], workspace=ws)
+    torch.cuda.synchronize()
+    v = sv.debug_views(ws, dims)
+    res = {"out": out.cpu().numpy(), "n": n.cpu().numpy(), "path": path.cpu().numpy(),
+           "logits": v["logits"].cpu().numpy(), "row_max": v["row_max"].cpu().numpy(),
+           "row_sumexp": v["row_sumexp"].cpu().numpy(), "status": v["status"].cpu().numpy()}
+    del ws, t
+    return res
+
+
+def compare_tree(x: dict, gpu: dict, ref=None) -> dict:
+    from oracle import tree_ref as TR
+    parent = [int(a) for a in x["parent"]]
+    B, T1, d = x["hidden_bits"].shape
+    if ref is None:
+        ref = TR.verify_tree(x["hidden_bits"], x["W_bits"], parent, x["tokens"], x["q"], x["uniforms"])
+    gl = gpu["logits"].astype(np.float64)
+    rl = ref.logits
+    dl = np.abs(gl - rl).max(axis=1)
+    assert np.all(dl <= LOGIT_RTOL * np.abs(rl).max(axis=1)), f"logit error {dl.max()}"
+    gp = np.exp(gl - gpu["row_max"].astype(np.float64)[:, None]) / \
+        gpu["row_sumexp"].astype(np.float64)[:, None]
+    dp = np.abs(gp - ref.p)
+    assert dp.max() <= P_ATOL, f"max |dp| = {dp.max()}"
+    rep = {"seqs": B, "max_abs_dlogit": float(dl.max()), "max_abs_dp": float(dp.max()),
+           "path_differs_flagged": 0, "draw_flagged": 0, "draw_flagged_exact": 0, "draw_exact": 0,
+           "mean_kept": float(gpu["n"].mean())}
+    flagged = ref.accept_flagged
+    for b in range(B):
+        n = int(gpu["n"][b])
+        path = [int(t) for t in gpu["path"][b, :n]]
+        assert all(int(t) == -1 for t in gpu["path"][b, n:]), f"seq {b}: path padding"
+        # a path of the tree carrying its nodes' tokens
+        prev = -1
+        for i, t in enumerate(path):
+            assert parent[t] == prev, f"seq {b}: node {t} is not a child of {prev}"
+            assert gpu["out"][b, i] == x["tokens"][b, t], f"seq {b}: kept token {i}"
+            prev = t
+        assert all(v == -1 for v in gpu["out"][b, n + 1:]), f"seq {b}: padding"
+        ref_path = [int(t) for t in ref.path_nodes[b, :int(ref.n_accepted[b])]]
+        if path != ref_path:
+            assert flagged[b], f"seq {b}: path {path} vs oracle {ref_path} with no flagged test"
+            rep["path_differs_flagged"] += 1
+            continue
+        y = int(gpu["out"][b, n])
+        if not ref.draw_flagged[b]:
+            assert y == ref.out_tokens[b, n], f"seq {b}: token {y} vs oracle {ref.out_tokens[b, n]}"
+            rep["draw_exact"] += 1
+        else:
+            rep["draw_flagged"] += 1
+            rep["draw_flagged_exact"] += int(y == ref.out_tokens[b, n])
+            u = float(x["uniforms"][b, T1 - 1])
+            assert R.draw_admissible(ref.draw_cdf[b], ref.draw_S[b], u, y), f"seq {b}: draw {y}"
+    return rep

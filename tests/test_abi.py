@@ -222,3 +222,56 @@ def test_sparse_head_argument_errors_return_before_launch():
     assert lib.sv_sparse_head(p, p, p, p, d, p, p, p, ctypes.c_void_p(FAKE + 16), n, None) == \
         _lib.SV_ERR_ALIGN
     assert lib.sv_sparse_head(p, p, p, p, d, p, p, p, p, n - 1, None) == _lib.SV_ERR_WORKSPACE
+
+
+def test_tree_shape_matches_the_oracle_topology():
+    from oracle import tree_ref as TR
+    from synth import inputs as I
+    import numpy as np
+    rng = np.random.default_rng(12)
+    trees = [[-1], list(range(-1, 7)), [-1, -1, 0, 0, 2, -1], I.EAGLE_LIKE_TREE]
+    trees += [[int(rng.integers(-1, t)) for t in range(int(rng.integers(1, 65)))] for _ in range(100)]
+    for parent in trees:
+        D, P, rounds = _lib.tree_shape(parent)
+        assert D == TR.max_depth(parent)
+        assert P == int((TR.q_slots(parent) >= 0).sum())
+        assert rounds == TR.worst_case_rounds(parent)
+    for bad in ([0], [-1, 1], [-1, -2], list(range(-1, 64)), []):
+        with pytest.raises(_lib.SVError):
+            _lib.tree_shape(bad)
+
+
+def test_tree_workspace_bytes():
+    d = _lib.Dims(2, 25, 1536, 262144)
+    assert _lib.tree_workspace_bytes(d) >= 2 * 26 * 262144 * 4
+    assert _lib.tree_workspace_bytes(_lib.Dims(2, 64, 64, 100)) > 0
+    assert _lib.tree_workspace_bytes(_lib.Dims(2, 65, 64, 100)) == 0
+    assert _lib.tree_workspace_bytes(_lib.Dims(0, 4, 64, 100)) == 0
+
+
+@no_device
+def test_tree_argument_errors_return_before_launch():
+    import numpy as np
+    lib = _lib.library()
+    parent = np.array([-1, -1, 0], dtype=np.int32)
+    pp = parent.ctypes.data_as(ctypes.c_void_p)
+    d = _lib.Dims(2, 3, 64, 1000)
+    n = _lib.tree_workspace_bytes(d)
+    p = ctypes.c_void_p(FAKE)
+    z = ctypes.c_void_p(0)
+    odd = ctypes.c_void_p(FAKE + 2)
+    # gamma must equal the node count: a 3-node parent array read as 4 nodes fails validation
+    bad_parent = np.array([-1, 1, 0, 0], dtype=np.int32)
+    assert lib.spec_verify_tree(p, p, bad_parent.ctypes.data_as(ctypes.c_void_p), p, p, p,
+                                _lib.Dims(2, 4, 64, 1000), p, p, None, p, n, None) == _lib.SV_ERR_DIMS
+    assert lib.spec_verify_tree(p, p, z, p, p, p, d, p, p, None, p, n, None) == _lib.SV_ERR_NULL
+    for k in (0, 1, 3, 4, 5, 7, 8, 10):
+        a = [p, p, pp, p, p, p, None, p, p, None, p]
+        a[k] = z
+        assert lib.spec_verify_tree(*a[:6], d, *a[7:], n, None) == _lib.SV_ERR_NULL, k
+    assert lib.spec_verify_tree(odd, p, pp, p, p, p, d, p, p, None, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_tree(p, p, pp, p, ctypes.c_void_p(FAKE + 4), p, d, p, p, None, p, n,
+                                None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_tree(p, p, pp, p, p, p, d, p, p, odd, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.spec_verify_tree(p, p, pp, p, p, p, d, p, p, None, p, n - 1, None) == \
+        _lib.SV_ERR_WORKSPACE

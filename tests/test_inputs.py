@@ -119,3 +119,19 @@ def test_clustered_head_inputs():
     for r in range(6):
         # drafts are members of some cluster
         assert np.isin(y["draft"][r // 3, r % 3], y["members"])
+
+
+def test_tree_inputs_draw_every_node_from_its_parents_q():
+    parent = [-1, -1, 0, 0, 2]
+    x = I.tree_inputs(3, parent, 16, 60, seed=4)
+    assert x["hidden_bits"].shape == (3, 6, 16) and x["tokens"].shape == (3, 5)
+    assert list(I.tree_rows_with_children(parent)) == [0, 1, 3]
+    assert x["q"].shape == (3, 3, 60) and x["uniforms"].shape == (3, 6)
+    np.testing.assert_allclose(x["q"].sum(-1), 1.0, atol=1e-5)
+    y = I.tree_repeated_trials(x, 2000, seed=5)
+    assert y["tokens"].shape == (2000, 5)
+    # node 4's parent is node 2 (row 3, q slot 2): its tokens follow that row
+    freq = np.bincount(y["tokens"][:, 4], minlength=60) / 2000
+    assert np.abs(freq - x["q"][0, 2]).max() < 0.05
+    for k, v in I.tree_inputs(3, parent, 16, 60, seed=4).items():
+        np.testing.assert_array_equal(v, x[k])
