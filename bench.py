@@ -1,6 +1,6 @@
 """Benchmark of the verification step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--mode sample|greedy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--mode MODE]
 
 One step is the whole path on one batch of resident synthetic inputs: the
 LM-head GEMM over all B*(gamma+1) rows (one pass over W), the softmax
@@ -13,9 +13,16 @@ that kernel's average duration for the roofline.  Prints one JSON line.
 Default workload: the Gemma-4-E2B-shaped head (d=1536, V=262144, gamma=4,
 B=1).  Other named workloads are in synth.inputs.CONFIGS.
 
---mode greedy times greedy (match) verification instead: spec_verify_greedy,
-whose LM-head launch keeps only argmax/softmax partials (no logits in HBM),
-then the per-sequence greedy kernel; events bracket the whole call.
+Other modes (same JSON line):
+  --mode greedy  greedy (match) verification: spec_verify_greedy, whose LM-head
+                 launch keeps only argmax/softmax partials (no logits in HBM),
+                 then the per-sequence greedy kernel; events bracket the call.
+  --mode sparse  verification with q given as (id, value) entries of its
+                 nonzeros (spec_verify_sparse_q); meant for --config sparse_q.
+  --mode tree    tree verification of a 25-node draft tree at the config's
+                 head shape and B (spec_verify_tree); events time the LM head.
+  --mode head    the drafter's clustered sparse head at the config's shape
+                 (sparse_q: B*gamma = 32 rows); value is rows/s.
 """
 
 from __future__ import annotations
@@ -90,7 +97,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gemma_e2b")
-    ap.add_argument("--mode", choices=("sample", "greedy"), default="sample")
+    ap.add_argument("--mode", choices=("sample", "greedy", "sparse", "tree", "head"),
+                    default="sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -117,40 +125,108 @@ def main():
     import draft_token_verification_02_amd as sv
     from synth import inputs
 
+    def upload(x):
+        # Through pinned host copies.  (Where a large tensor lands in HBM can
+        # move the LM-head time by ~10% at d = 4096; uploads from pageable
+        # host memory landed on the slow side more often in our measurements.)
+        return {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).pin_memory().to(dev)
+                .view(torch.bfloat16) if v.dtype == np.uint16 else
+                torch.from_numpy(np.ascontiguousarray(v)).pin_memory().to(dev)
+                for k, v in x.items()}
+
     cfg = inputs.CONFIGS[args.config]
-    x = inputs.generate(cfg)
-    # Upload through pinned host copies.  (Where a large tensor lands in HBM
-    # can move the LM-head time by ~10% at d = 4096; uploads from pageable
-    # host memory landed on the slow side more often in our measurements.)
-    t = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).pin_memory().to(dev).view(torch.bfloat16)
-         if v.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(v)).pin_memory().to(dev)
-         for k, v in x.items()}
-    hidden, W = t["hidden_bits"], t["W_bits"]
-    dims = sv.dims_of(hidden, W)
-    ws = sv.new_workspace(dims, dev)
-    out = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev)
-    n_acc = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
-    tgt = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev)
+    mode = args.mode
     stream = torch.cuda.current_stream(dev)
-    greedy = args.mode == "greedy"
+    extra_cfg = {}
+    if mode == "tree":
+        parent = inputs.EAGLE_LIKE_TREE
+        x = inputs.tree_inputs(cfg.B, parent, cfg.d, cfg.V, w_std=cfg.w_std, sigma=cfg.sigma,
+                               seed=cfg.seed)
+        t = upload({k: v for k, v in x.items() if k != "parent"})
+        T = len(parent)
+        D, P, rounds = sv.tree_shape(parent)
+        R = cfg.B * (T + 1)
+        dims = sv.Dims(cfg.B, T, cfg.d, cfg.V)
+        ws = torch.empty(sv.tree_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        out = torch.empty((cfg.B, D + 1), dtype=torch.int32, device=dev)
+        n_acc = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
+        path = torch.empty((cfg.B, D), dtype=torch.int32, device=dev)
+        extra_cfg = {"tree_nodes": T, "tree_depth": D, "tree_rounds": rounds}
 
-    def stage1():
-        if greedy:
-            sv.verify_greedy(hidden, W, t["draft"], out_tokens=out, n_accepted=n_acc,
-                             target_tokens=tgt, workspace=ws, stream=stream)
-        else:
-            sv.lmhead(hidden, W, ws, stream=stream)
+        def whole():
+            sv.verify_tree(t["hidden_bits"], t["W_bits"], parent, t["tokens"], t["q"],
+                           t["uniforms"], out_tokens=out, n_accepted=n_acc, path_nodes=path,
+                           workspace=ws, stream=stream)
 
-    def stage2():
-        if not greedy:
-            sv.accept_and_draw(dims, t["draft"], t["q"], t["uniforms"], out, n_acc, ws, stream=stream)
+        def lm_only():
+            sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream)
+    elif mode == "head":
+        if cfg.sparse is None:
+            raise SystemExit("--mode head needs a workload with clusters (e.g. --config sparse_q)")
+        C, M, k = cfg.sparse
+        N = cfg.B * cfg.gamma
+        x = inputs.clustered_head(N, cfg.d, cfg.V, C, M, w_std=cfg.w_std, seed=cfg.seed)
+        t = upload(x)
+        R = N
+        hd = sv.HeadDims(N, cfg.d, cfg.V, C, M, k)
+        ws = torch.empty(sv.sparse_head_workspace_bytes(hd), dtype=torch.uint8, device=dev)
+        qi = torch.empty((N, k * M), dtype=torch.int32, device=dev)
+        qv = torch.empty((N, k * M), dtype=torch.float32, device=dev)
+        cl = torch.empty((N, k), dtype=torch.int32, device=dev)
+        n_acc = None
+        extra_cfg = {"clusters": C, "cluster_size": M, "top_k": k, "head_rows": N}
 
-    def step():
-        stage1()
-        stage2()
+        def whole():
+            sv.sparse_head(t["h_bits"], t["W_bits"], t["centroid_bits"], t["members"], k,
+                           q_ids=qi, q_vals=qv, clusters=cl, workspace=ws, stream=stream)
+
+        lm_only = whole
+    else:
+        x = inputs.generate(cfg)
+        if mode == "sparse":
+            ids, vals = inputs.to_sparse_q(x["q"])
+            x = dict(x, q_ids=ids, q_vals=vals)
+            del x["q"]
+            extra_cfg = {"q_entries_per_row": int(ids.shape[-1])}
+        t = upload(x)
+        R = cfg.R
+        dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+        ws = sv.new_workspace(dims, dev)
+        out = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev)
+        n_acc = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
+        tgt = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev)
+
+        def lm_only():
+            if mode == "greedy":
+                sv.verify_greedy(t["hidden_bits"], t["W_bits"], t["draft"], out_tokens=out,
+                                 n_accepted=n_acc, target_tokens=tgt, workspace=ws, stream=stream)
+            else:
+                sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream)
+
+        def stage2():
+            if mode == "sample":
+                sv.accept_and_draw(dims, t["draft"], t["q"], t["uniforms"], out, n_acc, ws,
+                                   stream=stream)
+            elif mode == "sparse":
+                sv.accept_and_draw_sparse_q(dims, t["draft"], t["q_ids"], t["q_vals"],
+                                            t["uniforms"], out, n_acc, ws, stream=stream)
+
+        def whole():
+            lm_only()
+            stage2()
+
+    # For the event-timed loop: the LM-head launch alone, then the rest.
+    def event_step(e0, e1):
+        e0.record(stream)
+        lm_only()
+        e1.record(stream)
+        if mode in ("sample", "sparse"):
+            stage2()
+        elif mode == "tree":
+            whole()
 
     for _ in range(args.warmup):
-        step()
+        whole()
     torch.cuda.synchronize()
 
     # Timed region 1: K whole steps back to back -> value.
@@ -158,47 +234,59 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
-        step()
+        whole()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     # Timed region 2: K more steps with HIP events around each LM-head launch
     # (on the stream it runs on) -> the kernel's average duration.  Events
     # between the stages cost a few microseconds per step, so region 1 alone
-    # gives the throughput.
+    # gives the throughput.  (Tree mode: the LM-head launch is timed on its
+    # own, then the whole call runs, so region 2 is not a step time.)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(K):
-        ev[i][0].record(stream)
-        stage1()
-        ev[i][1].record(stream)
-        stage2()
+        event_step(*ev[i])
     torch.cuda.synchronize()
     elapsed_ev = time.perf_counter() - t1
     lm_ms = [a.elapsed_time(b) for a, b in ev]
-
-    n_host = n_acc.cpu().numpy()
-    R = cfg.R
-    ms_per_step = elapsed * 1e3 / K
-    n_rejected = int((n_host < cfg.gamma).sum())
-    if greedy:
-        step_bytes = perfmodel.greedy_step_bytes(cfg.B, cfg.gamma, cfg.d, cfg.V)
-        lm_bytes = step_bytes
-    else:
-        step_bytes = perfmodel.step_bytes(cfg.B, cfg.gamma, cfg.d, cfg.V, n_rejected)
-        lm_bytes = perfmodel.lmhead_bytes(cfg.B, cfg.gamma, cfg.d, cfg.V)
-    # R <= 64 rows: the streaming kernel, one launch per 64 rows; more rows:
-    # the LDS-tiled GEMM in one launch (when its partials fit, as in every
-    # named workload).  The achieved figure is the stage's algorithmic bytes
-    # (or flops) over the whole stage's time.
-    tiled = R > 64 and -(-cfg.V // 256) <= 1024
-    passes = 1 if tiled else -(-R // 64)
-    kernel = "lmhead_tiled_kernel" if tiled else "lmhead_kernel"
-    if greedy:
-        kernel += " + greedy_kernel"
     lm_avg_s = statistics.mean(lm_ms) * 1e-3
-    flops = perfmodel.lmhead_flops(cfg.B, cfg.gamma, cfg.d, cfg.V)
+
+    ms_per_step = elapsed * 1e3 / K
+    B, g, d, V = cfg.B, cfg.gamma, cfg.d, cfg.V
+    n_host = n_acc.cpu().numpy() if n_acc is not None else None
+    if mode == "head":
+        C, M, k = cfg.sparse
+        step_bytes = lm_bytes = perfmodel.sparse_head_bytes(R, d, C, M, k)
+        flops = perfmodel.sparse_head_flops(R, d, C, M, k)
+        kernel = "scores_kernel + topk_kernel + gather_kernel + qfinal_kernel"
+        passes = 1
+        tiled = False
+    else:
+        rows_g = R // B - 1                       # gamma, or T for a tree
+        lm_bytes = perfmodel.lmhead_bytes(B, rows_g, d, V)
+        flops = perfmodel.lmhead_flops(B, rows_g, d, V)
+        if mode == "greedy":
+            step_bytes = lm_bytes = perfmodel.greedy_step_bytes(B, g, d, V)
+        elif mode == "sparse":
+            step_bytes = perfmodel.sparse_q_step_bytes(B, g, d, V, int(t["q_ids"].shape[-1]),
+                                                       int((n_host < g).sum()))
+        elif mode == "tree":
+            path_h = path.cpu().numpy()
+            ends = [int(path_h[b, n_host[b] - 1]) if n_host[b] > 0 else -1 for b in range(B)]
+            n_res = sum(1 for e in ends if e in set(parent))   # last node has children
+            step_bytes = perfmodel.tree_step_bytes(B, rows_g, d, V, n_res)
+        else:
+            step_bytes = perfmodel.step_bytes(B, g, d, V, int((n_host < g).sum()))
+        # R <= 64 rows: the streaming kernel, one launch per 64 rows; more
+        # rows: the LDS-tiled GEMM in one launch (when its partials fit, as in
+        # every named workload).
+        tiled = R > 64 and -(-V // 256) <= 1024
+        passes = 1 if tiled else -(-R // 64)
+        kernel = "lmhead_tiled_kernel" if tiled else "lmhead_kernel"
+        if mode == "greedy":
+            kernel += " + greedy_kernel"
     # Bound by whichever roofline takes longer for the algorithmic work.
     mfma_bound = flops / perfmodel.MI355X_BF16_DENSE_FLOPS > lm_bytes / perfmodel.MI355X_HBM_BYTES_PER_S
     if mfma_bound:
@@ -210,15 +298,17 @@ def main():
         roof = {"bound": "hbm", "kernel": kernel, "achieved": lm_bytes / lm_avg_s / 1e9,
                 "peak": perfmodel.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] * 1e9 / perfmodel.MI355X_HBM_BYTES_PER_S
-    roof["traffic"] = None if greedy or tiled else traffic_from_counters(cfg.name)
+    roof["traffic"] = None if mode in ("greedy", "head") or tiled else traffic_from_counters(cfg.name)
     roof["alg_bytes_per_launch"] = lm_bytes // passes
     roof["hbm_GBps_alg"] = lm_bytes / lm_avg_s / 1e9
 
+    metric = ("verified positions/sec (fused LM-head + verify); LM-head HBM GB/s in roofline"
+              if mode != "head" else "drafter head rows/sec (clustered sparse LM head)")
     res = {
-        "metric": "verified positions/sec (fused LM-head + verify); LM-head HBM GB/s in roofline",
-        "mode": args.mode,
+        "metric": metric,
+        "mode": mode,
         "value": R * K / elapsed,
-        "unit": "positions/s",
+        "unit": "positions/s" if mode != "head" else "rows/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "ms_per_step_with_lmhead_events": elapsed_ev * 1e3 / K,
@@ -227,23 +317,28 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; W ~ N(0, 0.02^2), hidden ~ N(0, 1), q = softmax(logits + noise))"
-                + ("; greedy mode: the config's sampled drafts" if greedy else ""),
-        "config": {"workload": f"{cfg.name}: LM head d={cfg.d} V={cfg.V}, gamma={cfg.gamma}, B={cfg.B}",
-                   "B": cfg.B, "gamma": cfg.gamma, "d": cfg.d, "V": cfg.V, "sigma": cfg.sigma,
-                   "seed": cfg.seed, "rows": R, "parallelism": "single GPU"},
+                + {"greedy": "; greedy mode: the config's sampled drafts",
+                   "sparse": "; q given as (id, value) entries of its nonzeros",
+                   "tree": "; a 25-node draft tree, every node drawn from q at its parent",
+                   "head": "; drafter hidden rows ~ N(0, 1), disjoint random clusters"}.get(mode, ""),
+        "config": {"workload": f"{cfg.name}: LM head d={d} V={V}, gamma={g}, B={B}"
+                               + (f", {mode}" if mode != "sample" else ""),
+                   "B": B, "gamma": g, "d": d, "V": V, "sigma": cfg.sigma,
+                   "seed": cfg.seed, "rows": R, "parallelism": "single GPU", **extra_cfg},
         "steps_per_s": K / elapsed,
-        "emitted_tokens_per_s": float((n_host + 1).sum()) * K / elapsed,
         "step_alg_bytes": step_bytes,
         "step_GBps": step_bytes * K / elapsed / 1e9,
         "step_frac_hbm_peak": step_bytes * K / elapsed / perfmodel.MI355X_HBM_BYTES_PER_S,
         "lmhead_ms_avg": statistics.mean(lm_ms), "lmhead_ms_median": statistics.median(lm_ms),
         "lmhead_launches_per_step": passes,
-        "mfma_frac": flops / (statistics.mean(lm_ms) * 1e-3) / perfmodel.MI355X_BF16_DENSE_FLOPS,
+        "mfma_frac": flops / lm_avg_s / perfmodel.MI355X_BF16_DENSE_FLOPS,
         "roofline": roof,
-        "n_accepted": n_host.tolist()[:16],
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(x, greedy=greedy)
+    if n_host is not None:
+        res["emitted_tokens_per_s"] = float((n_host + 1).sum()) * K / elapsed
+        res["n_accepted"] = n_host.tolist()[:16]
+    if not args.no_cpu_baseline and mode in ("sample", "greedy"):
+        res["cpu_baseline"] = cpu_baseline(x, greedy=mode == "greedy")
     print(json.dumps(res), flush=True)
 
 

@@ -52,8 +52,9 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
                             int V, const int32_t* __restrict__ draft, QArg q,
                             const float* __restrict__ uniforms, float* r_m, float* r_s, int* flags) {
     __shared__ int s_n, s_flags;
-    __shared__ float s_qx[SPARSE ? SV_MAX_GAMMA : 1];
-    __shared__ int s_badq[SPARSE ? kBlock / kWave : 1];
+    __shared__ unsigned s_qx[SPARSE ? SV_MAX_GAMMA : 1];
+    __shared__ int s_x[SPARSE ? SV_MAX_GAMMA : 1];
+    __shared__ int s_badq;
     const int g1 = gamma + 1;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -71,24 +72,61 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
         }
     }
     if (SPARSE) {
-        // One wave per drafted position looks its token up in the q row.
-        bool badq = false;
-        for (int i = wave; i < gamma; i += kBlock / kWave) {
-            const int x = draft[(size_t)b * gamma + i];
-            const size_t row = ((size_t)b * gamma + i) * (size_t)q.K;
-            bool bad_id;
-            const float v = sparse_lookup(q.idx + row, q.val + row, q.K, x, V, &bad_id);
-            badq |= bad_id;
-            if (lane == 0) s_qx[i] = v;
+        // Every drafted position's token is looked up in its q row by the
+        // whole workgroup at once: the gamma rows' K ids are one flat range,
+        // 8 loads in flight per thread, and a match merges its value into
+        // s_qx by unsigned max on the (non-negative) value's bits.
+        if (threadIdx.x < SV_MAX_GAMMA) {
+            s_qx[threadIdx.x] = 0u;
+            s_x[threadIdx.x] = threadIdx.x < gamma ? draft[(size_t)b * gamma + threadIdx.x] : -1;
         }
-        if (lane == 0) s_badq[wave] = badq;
+        if (threadIdx.x == 0) s_badq = 0;
+        __syncthreads();
+        const int32_t* ids = q.idx + (size_t)b * gamma * q.K;
+        const float* vals = q.val + (size_t)b * gamma * q.K;
+        bool badq = false;
+        if ((q.K & 3) == 0) {
+            const int K4 = q.K >> 2;
+            const int total = gamma * K4;
+            const int4* id4 = reinterpret_cast<const int4*>(ids);
+            for (int e0 = 0; e0 < total; e0 += kBlock * 8) {
+                int4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + threadIdx.x + u * kBlock;
+                    v[u] = e < total ? id4[e] : make_int4(-1, -1, -1, -1);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + threadIdx.x + u * kBlock;
+                    if (e >= total) continue;
+                    const int i = e / K4;
+                    const int x = s_x[i];
+                    const int id[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        badq |= id[c] >= V;
+                        if (id[c] == x)
+                            atomicMax(&s_qx[i], __float_as_uint(sparse_value(vals[(size_t)e * 4 + c])));
+                    }
+                }
+            }
+        } else {
+            const int total = gamma * q.K;
+            for (int e = threadIdx.x; e < total; e += kBlock) {
+                const int id = ids[e];
+                const int i = e / q.K;
+                badq |= id >= V;
+                if (id == s_x[i]) atomicMax(&s_qx[i], __float_as_uint(sparse_value(vals[e])));
+            }
+        }
+        if (badq) atomicOr(&s_badq, 1);
     }
-
     merge_row_partials(part_max, part_sum, NP, NPs, (size_t)b * g1, g1, r_m, r_s);
     __syncthreads();
 
     if (wave == 0) {
-        if (SPARSE && lane < gamma) qx = s_qx[lane];
+        if (SPARSE && lane < gamma) qx = __uint_as_float(s_qx[lane]);
         bool keep = false;
         if (lane < gamma && valid) keep = ux * qx <= target_prob(lx, r_m[lane], r_s[lane]);
         const unsigned long long kept = __ballot(keep);
@@ -96,11 +134,7 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
         if (lane == 0) {
             s_n = min(__builtin_ctzll(~kept), gamma);
             int f = badm != 0 ? SV_DEV_BAD_DRAFT : 0;
-            if (SPARSE) {
-#pragma unroll
-                for (int w = 0; w < kBlock / kWave; ++w)
-                    if (s_badq[w]) f |= SV_DEV_BAD_QID;
-            }
+            if (SPARSE && s_badq) f |= SV_DEV_BAD_QID;
             s_flags = f;
         }
     }

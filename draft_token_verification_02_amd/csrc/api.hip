@@ -32,8 +32,8 @@ hipError_t launch_tree(const float* logits, const float* part_max, const float* 
                        int NPs, int B, int V, const TreeTopo& tp, int rounds,
                        const int32_t* tokens, const float* q, const float* uniforms, int NC,
                        double* csum, double* psum, float* row_max, float* row_sum, void* state,
-                       int32_t* out_tokens, int32_t* n_accepted, int32_t* path_nodes,
-                       int32_t* status, hipStream_t stream);
+                       int32_t* counters, int32_t* out_tokens, int32_t* n_accepted,
+                       int32_t* path_nodes, int32_t* status, hipStream_t stream);
 }  // namespace sv
 
 namespace {
@@ -374,8 +374,9 @@ sv_status spec_verify_tree(const uint16_t* hidden, const uint16_t* W_lmhead, con
         at<float>(workspace, L.part_sum), lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.V, tp,
         rounds, tree_tokens, q, uniforms, L.NC, at<double>(workspace, L.csum),
         at<double>(workspace, L.psum), at<float>(workspace, L.row_max),
-        at<float>(workspace, L.row_sum), at<char>(workspace, L.tstate), out_tokens, n_accepted,
-        path_nodes, at<int32_t>(workspace, L.status), s);
+        at<float>(workspace, L.row_sum), at<char>(workspace, L.tstate),
+        at<int32_t>(workspace, L.counters), out_tokens, n_accepted, path_nodes,
+        at<int32_t>(workspace, L.status), s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 

@@ -40,40 +40,6 @@ struct QArg {
 // pattern orders like the value (the LDS chunk merges entries by unsigned max).
 __device__ __forceinline__ float sparse_value(float v) { return v > 0.f ? v : 0.f; }
 
-// q of token x in one sparse row, by a whole wave: every lane scans its share
-// of the K ids (16-byte loads when the row allows), then a wave max.  Also
-// reports whether the row lists an id >= V.
-__device__ float sparse_lookup(const int32_t* __restrict__ ids, const float* __restrict__ vals, int K,
-                               int x, int V, bool* bad_id) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float best = 0.f;
-    bool bad = false;
-    if ((K & 3) == 0) {
-        const int4* id4 = reinterpret_cast<const int4*>(ids);
-        const int K4 = K >> 2;
-#pragma unroll 4
-        for (int j = lane; j < K4; j += kWave) {
-            const int4 v = id4[j];
-            bad |= v.x >= V || v.y >= V || v.z >= V || v.w >= V;
-            if (v.x == x) best = fmaxf(best, sparse_value(vals[4 * j + 0]));
-            if (v.y == x) best = fmaxf(best, sparse_value(vals[4 * j + 1]));
-            if (v.z == x) best = fmaxf(best, sparse_value(vals[4 * j + 2]));
-            if (v.w == x) best = fmaxf(best, sparse_value(vals[4 * j + 3]));
-        }
-    } else {
-#pragma unroll 4
-        for (int j = lane; j < K; j += kWave) {
-            const int id = ids[j];
-            bad |= id >= V;
-            if (id == x) best = fmaxf(best, sparse_value(vals[j]));
-        }
-    }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
-    *bad_id = __ballot(bad) != 0;
-    return best;
-}
-
 // Inclusive prefix sum of one double per thread over the workgroup, in a
 // fixed order (Hillis-Steele within each wave, then the wave totals added in
 // wave order).  Returns this thread's inclusive value; *total gets the sum,

@@ -8,18 +8,33 @@
 // 高效嵌入器 -- the LM head multiplies hidden states by the tied embedding
 // matrix W [V][d].
 //
-// Shape of the work.  At R in the hundreds the GEMM does 2*R flops per two
-// bytes of W, at or above the MI355X ridge (~312 flop/byte), so it is bound by
-// the MFMA pipes rather than HBM.  Each workgroup computes a 256 (vocab) x
-// 256 (hidden row) block with v_mfma_f32_16x16x32_bf16: 8 waves in a 2 x 4
-// arrangement, 128 x 64 per wave (8 x 4 fragments, accumulators in 128
-// registers).  K is walked in tiles of 64: both operand tiles are loaded from
-// global memory into registers one tile ahead, written to LDS (rows padded
-// to 144 bytes so the 16-byte fragment reads of 8 lanes hit distinct banks),
-// and read back as MFMA fragments; one barrier per tile.  W is the A operand
-// (vocab = M) and the hidden rows the B operand, so each lane ends with four
+// Shape of the work.  The GEMM does 2*R flops per two bytes of W: below the
+// MI355X ridge (~312 flop/byte) for R up to a few hundred, above it at
+// R = 1280.  Both kernels use v_mfma_f32_16x16x32_bf16 with W as the A
+// operand (vocab = M) and the hidden rows as B, so each lane ends with four
 // consecutive vocab entries of one hidden row -- a 16-byte logits store.
 //
+// 64 < R <= 128 (lmhead_mid_kernel): W-bandwidth bound.  A workgroup of four
+// waves computes a 256 (vocab) x 128 (row) block, each wave 64 vocab rows x
+// all 128 rows (4 x 8 fragments).  The operands travel differently:
+//   * W goes from memory straight into the MFMA A registers -- each lane
+//     loads 16 contiguous bytes of one vocab row per 32-wide k step, the
+//     fragment layout itself -- kept 8 k-steps ahead in a register ring
+//     whose slots are compile-time constants (a straight-line loop body), so
+//     each step waits only for its own loads;
+//   * the hidden rows, shared by every wave, are copied from memory straight
+//     into a four-stage LDS ring (global_load_lds_dwordx4), three 64-wide K
+//     tiles ahead, with one explicit wait and one barrier per tile.
+// Staging only the small operand in LDS keeps LDS traffic low, and W never
+// waits behind the hidden tile's loads in the in-order vmcnt queue.
+//
+// R > 128 (lmhead_big_kernel): MFMA bound at R = 1280.  256 x 256 blocks,
+// 8 waves of 128 x 64 (8 x 4 fragments); both operands staged through
+// registers into LDS per 64-wide K tile (rows padded to 144 bytes so the
+// 16-byte fragment reads of 8 lanes hit distinct banks), one tile ahead.
+// The larger block halves the L2 traffic per flop of a 128-row block, which
+// is what bounds the many-row case.
+
 // Block order.  Workgroups are dispatched round-robin over the 8 XCDs; the
 // block index is remapped so that each XCD receives a contiguous run of the
 // (vocab block, row block) sequence with row blocks fastest.  The row blocks
@@ -32,30 +47,34 @@ namespace sv {
 
 namespace {
 
-constexpr int kTV = kLmTiledVocab;   // vocab rows per workgroup
-constexpr int kTR = 256;             // hidden rows per workgroup
+constexpr int kTV = kLmTiledVocab;   // vocab rows per workgroup (256)
 constexpr int kTK = 64;              // k per LDS tile
-constexpr int kTWaves = 8;
-constexpr int kTThreads = kTWaves * kWave;
-constexpr int kWaveV = 128, kWaveR = 64;           // per-wave block
-constexpr int kFV = kWaveV / kLmTile, kFR = kWaveR / kLmTile;   // 8 x 4 fragments
+constexpr int kTThreads = 4 * kWave;
 constexpr int kRowBytes = kTK * 2 + 16;            // padded LDS row: 144 bytes
 constexpr int kXcds = 8;
 
-static_assert((kTV / kWaveV) * (kTR / kWaveR) == kTWaves, "wave grid");
+// ---------------------------------------------------------------------------
+// R > 128: 256 x 256 blocks, 8 waves of 128 x 64, both operands staged in LDS.
+constexpr int kBigTR = 256;          // hidden rows per workgroup
+constexpr int kBigWaves = 8;
+constexpr int kBigThreads = kBigWaves * kWave;
+constexpr int kWaveV = 128, kWaveR = 64;           // per-wave block
+constexpr int kFV = kWaveV / kLmTile, kFR = kWaveR / kLmTile;   // 8 x 4 fragments
+
+static_assert((kTV / kWaveV) * (kBigTR / kWaveR) == kBigWaves, "wave grid");
 
 // One K tile of both operands: 256 rows x 64 bf16 each = 2048 chunks of 16
 // bytes per operand, 4 per thread.
-struct Stage {
+struct BigStage {
     u32x4 w[4], h[4];
 };
 
-__device__ __forceinline__ void load_stage(Stage& s, const uint16_t* __restrict__ W,
+__device__ __forceinline__ void big_load_stage(BigStage& s, const uint16_t* __restrict__ W,
                                            const uint16_t* __restrict__ H, int v0, int r0, int k0,
                                            int V, int R, int d) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int c = threadIdx.x + j * kTThreads;      // chunk 0..2047
+        const int c = threadIdx.x + j * kBigThreads;      // chunk 0..2047
         const int row = c >> 3, col = (c & 7) * 8;      // 8 chunks per 64-element row
         const int k = k0 + col;
         const int v = min(v0 + row, V - 1);             // past the end: a valid row, never stored
@@ -70,27 +89,27 @@ __device__ __forceinline__ void load_stage(Stage& s, const uint16_t* __restrict_
     }
 }
 
-__device__ __forceinline__ void store_stage(const Stage& s, char* lw, char* lh) {
+__device__ __forceinline__ void big_store_stage(const BigStage& s, char* lw, char* lh) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int c = threadIdx.x + j * kTThreads;
+        const int c = threadIdx.x + j * kBigThreads;
         const int row = c >> 3, col = c & 7;
         *reinterpret_cast<u32x4*>(lw + row * kRowBytes + col * 16) = s.w[j];
         *reinterpret_cast<u32x4*>(lh + row * kRowBytes + col * 16) = s.h[j];
     }
 }
 
-__global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
+__global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
     float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
     int32_t* __restrict__ counters, int n_counters) {
     // LDS: two stages of (W tile, hidden tile), each 256 rows x 144 bytes.
     __shared__ __attribute__((aligned(16))) char lds[2][2][kTV * kRowBytes];
-    __shared__ float s_max[kTV / kWaveV][kTR];
-    __shared__ float s_sum[kTV / kWaveV][kTR];
-    __shared__ float s_av[kTV / kWaveV][kTR];
-    __shared__ int s_ai[kTV / kWaveV][kTR];
+    __shared__ float s_max[kTV / kWaveV][kBigTR];
+    __shared__ float s_sum[kTV / kWaveV][kBigTR];
+    __shared__ float s_av[kTV / kWaveV][kBigTR];
+    __shared__ int s_ai[kTV / kWaveV][kBigTR];
 
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
         counters[i] = 0;
@@ -102,7 +121,7 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
     const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nblocks) return;          // padding blocks of the rounded-up grid
     const int vb = logical / nrb, rb = logical % nrb;
-    const int v0 = vb * kTV, r0 = rb * kTR;
+    const int v0 = vb * kTV, r0 = rb * kBigTR;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -116,13 +135,13 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
         for (int b = 0; b < kFR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (d + kTK - 1) / kTK;
-    Stage st;
-    load_stage(st, W, hidden, v0, r0, 0, V, R, d);
-    store_stage(st, lds[0][0], lds[0][1]);
+    BigStage st;
+    big_load_stage(st, W, hidden, v0, r0, 0, V, R, d);
+    big_store_stage(st, lds[0][0], lds[0][1]);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) load_stage(st, W, hidden, v0, r0, (kt + 1) * kTK, V, R, d);
+        if (kt + 1 < nk) big_load_stage(st, W, hidden, v0, r0, (kt + 1) * kTK, V, R, d);
         const char* lw = lds[cur][0] + (wv * kWaveV + r16) * kRowBytes + kg * 16;
         const char* lh = lds[cur][1] + (wr * kWaveR + r16) * kRowBytes + kg * 16;
 #pragma unroll
@@ -142,7 +161,7 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
                         __builtin_bit_cast(bf16x8, fa[a]), __builtin_bit_cast(bf16x8, fb[b]),
                         acc[a][b], 0, 0, 0);
         }
-        if (kt + 1 < nk) store_stage(st, lds[cur ^ 1][0], lds[cur ^ 1][1]);
+        if (kt + 1 < nk) big_store_stage(st, lds[cur ^ 1][0], lds[cur ^ 1][1]);
         __syncthreads();
     }
 
@@ -201,7 +220,7 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
         if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; s_av[wv][rl] = av; s_ai[wv][rl] = ai; }
     }
     __syncthreads();
-    if (threadIdx.x < kTR && r0 + (int)threadIdx.x < R) {
+    if (threadIdx.x < kBigTR && r0 + (int)threadIdx.x < R) {
         const int rl = threadIdx.x;
         float m = -INFINITY, s = 0.f, av = -INFINITY;
         int ai = -1;
@@ -216,16 +235,366 @@ __global__ __launch_bounds__(kTThreads) void lmhead_tiled_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// 64 < R <= 128: 256 x 128 blocks, W straight into registers, hidden rows in LDS.
+// s_waitcnt vmcnt(N), the other counters untouched (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The pipelined path keeps four hidden-tile stages in LDS.
+constexpr int kStages = 4;
+
+// vmcnt to wait for before reading tile kt's stage, counted in this wave's
+// vector-memory operations issued after that tile's copies (issued S - 1
+// tiles earlier): the copies and A refills of the S - 2 tiles in between,
+// but not the refills of the copy's own tile.  h = -1: a tile of the main
+// loop (every tile copies CHD chunks and refills 2 * FV registers); h >= 0:
+// tile h of the last group, where only tile 0 still copies and only the
+// k-steps 2h + s with 2h + s + U < 2S still refill.
+template <int S, int U, int CHD, int FV>
+constexpr int tail_wait(int h) {
+    auto ops = [](int t) {                    // operations of last-group tile t
+        int n = t == 0 ? CHD : 0;
+        for (int s = 0; s < 2; ++s) n += (2 * t + s + U < 2 * S) ? FV : 0;
+        return n;
+    };
+    const int main_ops = CHD + 2 * FV;
+    if (h < 0) return (S - 2) * main_ops;
+    int n = 0;
+    if (h <= S - 2) {
+        n = (S - 2 - h) * main_ops;
+        for (int t = 0; t < h; ++t) n += ops(t);
+    } else {
+        for (int t = 1; t <= S - 2; ++t) n += ops(t);
+    }
+    return n;
+}
+
+template <int FV, int FR, int WV, int WR, int U, bool FAST>
+__global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
+    int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
+    float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
+    int32_t* __restrict__ counters, int n_counters) {
+    constexpr int TR = kLmTile * FR * WR;             // rows per workgroup
+    constexpr int kWaveV = kLmTile * FV;
+    constexpr int kWaveR = kLmTile * FR;
+    constexpr int CH = TR * (kTK / 8) / kTThreads;    // 16-byte hidden chunks per thread per tile
+    static_assert(WV * WR == 4 && kWaveV * WV == kTV, "wave grid");
+    static_assert(!FAST || ((U == 4 || U == 8) && FR % 8 == 0), "ring depth and fragment groups");
+
+    // FAST: four stages of TR x 128 bytes (swizzled), each its own array so
+    // that the compiler can tell a stage being read from the stages the
+    // copies are filling; otherwise two buffers of TR x 144 bytes (padded).
+    constexpr int kStageBytes = FAST ? TR * 128 : TR * kRowBytes;
+    __shared__ __attribute__((aligned(16))) char lds0[kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds1[kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds2[FAST ? kStageBytes : 16];
+    __shared__ __attribute__((aligned(16))) char lds3[FAST ? kStageBytes : 16];
+    __shared__ float s_max[WV][TR];
+    __shared__ float s_sum[WV][TR];
+    __shared__ float s_av[WV][TR];
+    __shared__ int s_ai[WV][TR];
+
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
+        counters[i] = 0;
+
+    // XCD-aware block order: hardware block b runs on XCD b % 8; give each XCD
+    // a contiguous run of logical blocks, row blocks fastest.
+    const int nblocks = nvb * nrb;
+    const int per_xcd = (nblocks + kXcds - 1) / kXcds;
+    const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (logical >= nblocks) return;          // padding blocks of the rounded-up grid
+    const int vb = logical / nrb, rb = logical % nrb;
+    const int v0 = vb * kTV, r0 = rb * TR;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wv = wave % WV, wr = wave / WV;
+    const int r16 = lane & 15, kg = lane >> 4;
+
+    // A: this lane's vocab row of each fragment (past V: a valid row, never stored)
+    const uint16_t* ap[FV];
+#pragma unroll
+    for (int a = 0; a < FV; ++a) {
+        const int v = min(v0 + wv * kWaveV + a * kLmTile + r16, V - 1);
+        ap[a] = W + (size_t)v * d + kg * 8;
+    }
+    const int nsteps = (d + 31) / 32;
+    const u32x4 zero{0u, 0u, 0u, 0u};
+    u32x4 ar[U][FV];
+    auto load_a = [&](int slot, int ks) {
+#pragma unroll
+        for (int a = 0; a < FV; ++a) {
+            if (FAST) ar[slot][a] = *reinterpret_cast<const u32x4*>(ap[a] + ks * 32);
+            else ar[slot][a] = ks * 32 + kg * 8 < d ? *reinterpret_cast<const u32x4*>(ap[a] + ks * 32)
+                                                    : zero;
+        }
+    };
+
+    // B: the hidden tile, CH 16-byte chunks per thread (8 per 64-wide row)
+    u32x4 hb[CH];
+    auto load_b = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = threadIdx.x + j * kTThreads;
+            const int row = c >> 3, col = (c & 7) * 8;
+            const int r = min(r0 + row, R - 1);          // pad rows repeat the last row
+            if (FAST || k0 + col < d) hb[j] = *reinterpret_cast<const u32x4*>(hidden + (size_t)r * d + k0 + col);
+            else hb[j] = zero;
+        }
+    };
+    auto store_b = [&](char* l) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = threadIdx.x + j * kTThreads;
+            const int row = c >> 3, col = c & 7;
+            *reinterpret_cast<u32x4*>(l + row * kRowBytes + col * 16) = hb[j];
+        }
+    };
+
+    f32x4 acc[FV][FR];
+#pragma unroll
+    for (int a = 0; a < FV; ++a)
+#pragma unroll
+        for (int b = 0; b < FR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (d + kTK - 1) / kTK;
+    auto mfma_step = [&](const char* lh, int s, int slot) {
+        u32x4 fb[FR];
+#pragma unroll
+        for (int b = 0; b < FR; ++b)
+            fb[b] = *reinterpret_cast<const u32x4*>(lh + b * kLmTile * kRowBytes + s * 64);
+#pragma unroll
+        for (int a = 0; a < FV; ++a)
+#pragma unroll
+            for (int b = 0; b < FR; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, ar[slot][a]), __builtin_bit_cast(bf16x8, fb[b]),
+                    acc[a][b], 0, 0, 0);
+    };
+    const int lrow = (wr * kWaveR + r16) * kRowBytes + kg * 16;
+
+    if constexpr (FAST) {
+        // The hidden tile goes from memory straight into LDS
+        // (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS,
+        // 16 bytes per lane), into a ring of kStages tiles filled
+        // kStages - 1 tiles ahead; no registers hold it on the way.  A
+        // 64-wide row is 8 chunks of 16 bytes; chunk g of row r sits in slot
+        // g ^ (r & 7), so the fragment reads of 8 consecutive rows at one
+        // chunk hit distinct banks.  The compiler does not track these
+        // copies, so each tile waits for its own explicitly: vmcnt counts
+        // this wave's vector-memory operations in issue order, and the
+        // straight-line loop fixes how many were issued after a tile's copy
+        // (tail_wait; the A refills issued in the copy's own tile are not
+        // counted, which only makes the wait stronger); a bare s_barrier then
+        // makes every wave's part visible.  The loop body covers kStages
+        // tiles, so stages and ring slots are compile-time constants.
+        constexpr int S = kStages;
+        constexpr int CHD = TR * 8 / kTThreads;            // copies per thread per tile
+        auto stage = [&](int st) { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
+        auto copy_b = [&](int kt, int st) {
+#pragma unroll
+            for (int j = 0; j < CHD; ++j) {
+                const int blk = j * 4 + wave;                // 1 KB block of the stage
+                const int c = blk * kWave + lane;
+                const int row = c >> 3, g = (c & 7) ^ (row & 7);
+                const int r = min(r0 + row, R - 1);          // pad rows repeat the last row
+                __builtin_amdgcn_global_load_lds(
+                    hidden + (size_t)r * d + kt * kTK + g * 8,
+                    (__attribute__((address_space(3))) void*)(stage(st) + blk * 1024), 16, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        const int brow = (wr * kWaveR + r16) * 128;
+        const int off0 = ((0 * 4 + kg) ^ (r16 & 7)) * 16, off1 = ((1 * 4 + kg) ^ (r16 & 7)) * 16;
+        auto step_dma = [&](int st, int s, int slot) {
+            const char* lh = stage(st) + brow + (s ? off1 : off0);
+            // B fragments eight at a time (register budget), each used by all FV
+#pragma unroll
+            for (int b0 = 0; b0 < FR; b0 += 8) {
+                u32x4 fb[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    fb[b] = *reinterpret_cast<const u32x4*>(lh + (b0 + b) * kLmTile * 128);
+#pragma unroll
+                for (int a = 0; a < FV; ++a)
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        acc[a][b0 + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, ar[slot][a]), __builtin_bit_cast(bf16x8, fb[b]),
+                            acc[a][b0 + b], 0, 0, 0);
+            }
+        };
+
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t) copy_b(t, t);
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_a(u, u);
+        int kt0 = 0;
+        for (; kt0 < nk - S; kt0 += S) {
+#pragma unroll
+            for (int h = 0; h < S; ++h) {
+                const int kt = kt0 + h;
+                wait_vmcnt<tail_wait<S, U, CHD, FV>(-1)>();
+                __builtin_amdgcn_s_barrier();
+                copy_b(kt + S - 1, (h + S - 1) % S);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    step_dma(h, s, (h * 2 + s) % U);
+                    load_a((h * 2 + s) % U, kt * 2 + s + U);
+                }
+            }
+        }
+        // The last group: the copy for the last tile, refills only while
+        // k-steps remain, then nothing.
+#pragma unroll
+        for (int h = 0; h < S; ++h) {
+            const int kt = kt0 + h;
+            if (h == 0) wait_vmcnt<tail_wait<S, U, CHD, FV>(0)>();
+            else if (h == 1) wait_vmcnt<tail_wait<S, U, CHD, FV>(1)>();
+            else if (h == 2) wait_vmcnt<tail_wait<S, U, CHD, FV>(2)>();
+            else wait_vmcnt<tail_wait<S, U, CHD, FV>(3)>();
+            __builtin_amdgcn_s_barrier();
+            if (h == 0) copy_b(kt + S - 1, S - 1);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                step_dma(h, s, (h * 2 + s) % U);
+                if (h * 2 + s + U < 2 * S) load_a((h * 2 + s) % U, kt * 2 + s + U);
+            }
+        }
+    } else {
+        // Any d (a multiple of 8): a two-deep ring, guarded loads.
+        auto buf = [&](int i) { return i ? lds1 : lds0; };
+        load_b(0);
+        load_a(0, 0);
+        if (1 < nsteps) load_a(1, 1);
+        store_b(buf(0));
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) load_b((kt + 1) * kTK);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ks = kt * 2 + s;
+                if (ks < nsteps) {
+                    mfma_step(buf(cur) + lrow, s, s);
+                    if (ks + 2 < nsteps) load_a(s, ks + 2);
+                }
+            }
+            if (kt + 1 < nk) store_b(buf(cur ^ 1));
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: lane holds D[vocab 4*kg + i][row r16] of each fragment; its
+    // ids rise with a and i, so a strict '>' keeps the first maximum.
+    const bool vec_store = (V & 3) == 0;
+#pragma unroll
+    for (int b = 0; b < FR; ++b) {
+        const int rl = wr * kWaveR + b * kLmTile + r16;     // row within the block
+        const int r = r0 + rl;
+        const bool row_ok = r < R;
+        float* lrow = logits ? logits + (size_t)(row_ok ? r : 0) * V : nullptr;
+        float mx = -INFINITY, av = -INFINITY;
+        int ai = -1;
+#pragma unroll
+        for (int a = 0; a < FV; ++a) {
+            const int v = v0 + wv * kWaveV + a * kLmTile + kg * 4;
+            if (row_ok && lrow) {
+                if (vec_store) {
+                    if (v < V) __builtin_nontemporal_store(acc[a][b], reinterpret_cast<f32x4*>(lrow + v));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (v + i < V) lrow[v + i] = acc[a][b][i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (v + i < V) {
+                    mx = fmaxf(mx, acc[a][b][i]);
+                    if (acc[a][b][i] > av) { av = acc[a][b][i]; ai = v + i; }
+                }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+        for (int off = 16; off < kWave; off <<= 1) {
+            const float av2 = __shfl_xor(av, off);
+            const int ai2 = __shfl_xor(ai, off);
+            arg_merge(av, ai, av2, ai2);
+        }
+        float sm = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+            for (int a = 0; a < FV; ++a) {
+                const int v = v0 + wv * kWaveV + a * kLmTile + kg * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (v + i < V) sm += expf(acc[a][b][i] - mx);
+            }
+        }
+        sm += __shfl_xor(sm, 16);
+        sm += __shfl_xor(sm, 32);
+        if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; s_av[wv][rl] = av; s_ai[wv][rl] = ai; }
+    }
+    __syncthreads();
+    for (int rl = threadIdx.x; rl < TR; rl += kTThreads) {
+        if (r0 + rl >= R) break;
+        float m = -INFINITY, s = 0.f, av = -INFINITY;
+        int ai = -1;
+#pragma unroll
+        for (int w = 0; w < WV; ++w) {
+            lse_merge(m, s, s_max[w][rl], s_sum[w][rl]);
+            arg_merge(av, ai, s_av[w][rl], s_ai[w][rl]);
+        }
+        part_max[(size_t)(r0 + rl) * NPs + vb] = m;
+        part_sum[(size_t)(r0 + rl) * NPs + vb] = s;
+        part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
+    }
+}
+
+
+template <int FV, int FR, int WV, int WR, int U>
+hipError_t launch_shape(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
+                        float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+                        int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
+    constexpr int TR = kLmTile * FR * WR;
+    const int nvb = lmhead_tiled_partials(V);
+    const int nrb = (R + TR - 1) / TR;
+    const int nblocks = nvb * nrb;
+    const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
+    // pipelined: d a multiple of 4 tiles of 64, at least two groups of them
+    if (d % (kTK * kStages) == 0 && d / (kTK * kStages) >= 2)
+        lmhead_mid_kernel<FV, FR, WV, WR, U, true><<<dim3(grid), dim3(kTThreads), 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
+            n_counters);
+    else
+        lmhead_mid_kernel<FV, FR, WV, WR, 2, false><<<dim3(grid), dim3(kTThreads), 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
+            n_counters);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
                                float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                                int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
+    if (R <= 128)
+        return launch_shape<4, 8, 4, 1, 8>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+                                           NPs, counters, n_counters, stream);
     const int nvb = lmhead_tiled_partials(V);
-    const int nrb = (R + kTR - 1) / kTR;
+    const int nrb = (R + kBigTR - 1) / kBigTR;
     const int nblocks = nvb * nrb;
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
-    lmhead_tiled_kernel<<<dim3(grid), dim3(kTThreads), 0, stream>>>(
+    lmhead_big_kernel<<<dim3(grid), dim3(kBigThreads), 0, stream>>>(
         hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     return hipGetLastError();
 }

@@ -30,7 +30,9 @@
 //                      sequence's current row (nothing for finished ones);
 //   tree_decide_kernel one workgroup per sequence: S from the totals, then
 //                      either the pending sibling test and the walk onwards,
-//                      or the inverse-CDF pick that ends the sequence.
+//                      or the inverse-CDF pick that ends the sequence;
+//   or, with at most 64 chunk workgroups in all, tree_round_kernel: both in
+//   one launch, the sequence's last chunk workgroup deciding.
 // The state of each walk lives in the workspace between launches.
 
 #include "draw_common.h"
@@ -165,14 +167,12 @@ __global__ __launch_bounds__(kBlock) void tree_init_kernel(
     }
 }
 
-// Chunk totals of the weights at the sequence's current row: max(0, p - c q)
-// (the residual of a pending test, or the draw's), or p for a bonus draw.
-__global__ __launch_bounds__(kBlock) void tree_sums_kernel(
-    TreeTopo tp, TreeArgs a, const TreeState* __restrict__ state, int NC,
-    double* __restrict__ csum, double* __restrict__ psum) {
-    const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
-    const TreeState st = state[b];
-    if (st.phase == kPhaseDone) return;
+// Chunk c's totals of the weights at the sequence's current row:
+// max(0, p - c q) (the residual of a pending test, or the draw's), or p for a
+// bonus draw.  Every thread takes part; thread 0 stores them.
+__device__ void tree_chunk_totals(const TreeState& st, const TreeTopo& tp, int b, int c, int NC,
+                                  const TreeArgs& a, double* __restrict__ csum,
+                                  double* __restrict__ psum) {
     const DrawRow d = tree_draw_row(st, tp, b, a);
     const int cs = c * kDrawChunk;
     float w[kDrawPerThread], p[kDrawPerThread];
@@ -189,14 +189,15 @@ __global__ __launch_bounds__(kBlock) void tree_sums_kernel(
     }
 }
 
-__global__ __launch_bounds__(kBlock) void tree_decide_kernel(
-    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, const double* __restrict__ csum,
-    const double* __restrict__ psum, int32_t* __restrict__ n_accepted,
-    int32_t* __restrict__ status) {
+// With every chunk total of the round in place: the sum S, then either the
+// pending sibling test and the walk onwards (state updated for the next
+// round), or the inverse-CDF pick that ends the sequence.  Every thread takes
+// part (the pick is a workgroup operation).
+__device__ void tree_decide(TreeState st, const TreeTopo& tp, int b, const TreeArgs& a, int NC,
+                            const double* __restrict__ csum, const double* __restrict__ psum,
+                            TreeState* __restrict__ state, int32_t* __restrict__ n_accepted,
+                            int32_t* __restrict__ status) {
     __shared__ int s_draw;
-    const int b = blockIdx.x;
-    TreeState st = state[b];
-    if (st.phase == kPhaseDone) return;
     const DrawRow d = tree_draw_row(st, tp, b, a);
     // S in the association the pick uses (thread-owned runs of chunks, then a scan)
     const int per = (NC + kBlock - 1) / kBlock;
@@ -230,23 +231,80 @@ __global__ __launch_bounds__(kBlock) void tree_decide_kernel(
     }
 }
 
+// Split round, many sequences: chunk totals here, tree_decide_kernel next
+// (the kernel boundary orders the totals before the decision).
+__global__ __launch_bounds__(kBlock) void tree_sums_kernel(
+    TreeTopo tp, TreeArgs a, const TreeState* __restrict__ state, int NC,
+    double* __restrict__ csum, double* __restrict__ psum) {
+    const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
+    const TreeState st = state[b];
+    if (st.phase == kPhaseDone) return;
+    tree_chunk_totals(st, tp, b, c, NC, a, csum, psum);
+}
+
+__global__ __launch_bounds__(kBlock) void tree_decide_kernel(
+    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, const double* __restrict__ csum,
+    const double* __restrict__ psum, int32_t* __restrict__ n_accepted,
+    int32_t* __restrict__ status) {
+    const int b = blockIdx.x;
+    const TreeState st = state[b];
+    if (st.phase == kPhaseDone) return;
+    tree_decide(st, tp, b, a, NC, csum, psum, state, n_accepted, status);
+}
+
+// Fused round, few sequences: the sequence's last chunk workgroup to finish
+// (a per-sequence counter that the LM-head launch zeroes and this kernel
+// resets) decides -- one launch per round.
+__global__ __launch_bounds__(kBlock) void tree_round_kernel(
+    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, double* __restrict__ csum,
+    double* __restrict__ psum, int32_t* __restrict__ counters, int32_t* __restrict__ n_accepted,
+    int32_t* __restrict__ status) {
+    __shared__ int s_last;
+    const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
+    const TreeState st = state[b];
+    if (st.phase == kPhaseDone) return;
+    tree_chunk_totals(st, tp, b, c, NC, a, csum, psum);
+    if (threadIdx.x == 0) {
+        __threadfence();                       // publish the totals before counting
+        s_last = atomicAdd(&counters[b], 1) == NC - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();                           // see every other chunk's totals
+    if (threadIdx.x == 0) counters[b] = 0;     // ready for the next round
+    tree_decide(st, tp, b, a, NC, csum, psum, state, n_accepted, status);
+}
+
 }  // namespace
+
+#ifndef SV_TREE_FUSE_MAX_GROUPS
+#define SV_TREE_FUSE_MAX_GROUPS 64
+#endif
 
 hipError_t launch_tree(const float* logits, const float* part_max, const float* part_sum, int NP,
                        int NPs, int B, int V, const TreeTopo& tp, int rounds,
                        const int32_t* tokens, const float* q, const float* uniforms, int NC,
                        double* csum, double* psum, float* row_max, float* row_sum, void* state,
-                       int32_t* out_tokens, int32_t* n_accepted, int32_t* path_nodes,
-                       int32_t* status, hipStream_t stream) {
+                       int32_t* counters, int32_t* out_tokens, int32_t* n_accepted,
+                       int32_t* path_nodes, int32_t* status, hipStream_t stream) {
     TreeArgs a{logits, row_max, row_sum, tokens, q, uniforms, V, out_tokens, path_nodes};
     TreeState* st = static_cast<TreeState*>(state);
     tree_init_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(part_max, part_sum, NP, NPs, tp, a,
                                                           row_max, row_sum, st, n_accepted,
                                                           status);
     hipError_t e = hipGetLastError();
+    const unsigned groups = (unsigned)B * NC;
+    // Few chunk workgroups: one fused launch per round (see draw_kernel for
+    // why many sequences use the split form instead).
+    const bool fused = groups <= SV_TREE_FUSE_MAX_GROUPS;
     for (int r = 0; r < rounds && e == hipSuccess; ++r) {
-        tree_sums_kernel<<<dim3((unsigned)B * NC), dim3(kBlock), 0, stream>>>(tp, a, st, NC, csum,
-                                                                             psum);
+        if (fused) {
+            tree_round_kernel<<<dim3(groups), dim3(kBlock), 0, stream>>>(
+                tp, a, st, NC, csum, psum, counters, n_accepted, status);
+            e = hipGetLastError();
+            continue;
+        }
+        tree_sums_kernel<<<dim3(groups), dim3(kBlock), 0, stream>>>(tp, a, st, NC, csum, psum);
         e = hipGetLastError();
         if (e != hipSuccess) break;
         tree_decide_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(tp, a, st, NC, csum, psum,

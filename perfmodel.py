@@ -73,3 +73,40 @@ def greedy_step_bytes(B: int, gamma: int, d: int, V: int) -> int:
     R = rows(B, gamma)
     small = 4 * B * gamma + 4 * B * (gamma + 1) * 2 + 4 * B
     return 2 * V * d + 2 * R * d + small
+
+
+def sparse_q_step_bytes(B: int, gamma: int, d: int, V: int, K: int, n_rejected: int) -> int:
+    """Minimum HBM bytes of verification with sparse q: as step_bytes, but a
+    rejected sequence reads its q row's K (id, value) entries instead of V
+    floats, and the accept tests' lookups read each drafted row's K entries."""
+    R = rows(B, gamma)
+    small = 4 * B * gamma * 2 + 4 * B * (gamma + 1) * 2 + 4 * B
+    return (lmhead_bytes(B, gamma, d, V) + 4 * B * V + 8 * K * (B * gamma + n_rejected)
+            + small)
+
+
+def tree_lmhead_bytes(B: int, T: int, d: int, V: int) -> int:
+    """LM-head bytes of tree verification: one row per node plus the root."""
+    return lmhead_bytes(B, T, d, V)
+
+
+def tree_step_bytes(B: int, T: int, d: int, V: int, n_residual: int) -> int:
+    """Minimum HBM bytes of tree verification: the LM head over B*(T+1) rows,
+    the drawn row's logits per sequence and its q row when the draw is from a
+    residual (n_residual sequences), plus the per-node gathers and outputs.
+    Sums for rejected siblings before the last are extra passes over a row
+    that this lower bound leaves out."""
+    small = 4 * B * T * 3 + 4 * B * (T + 1) + 8 * B
+    return lmhead_bytes(B, T, d, V) + 4 * B * V + 4 * V * n_residual + small
+
+
+def sparse_head_bytes(N: int, d: int, C: int, M: int, k: int) -> int:
+    """Minimum HBM bytes of the clustered head for N rows: the cluster table
+    once, every chosen token's W row once per row that chose it, the hidden
+    rows, the members of the chosen clusters, and the (id, q) outputs."""
+    K = k * M
+    return 2 * C * d + 2 * N * K * d + 2 * N * d + 4 * N * K + 8 * N * K
+
+
+def sparse_head_flops(N: int, d: int, C: int, M: int, k: int) -> int:
+    return 2 * N * d * (C + k * M)

@@ -65,6 +65,8 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (40, 7, 24, 65, 8),        # R = 320
     (1, 4, 4096, 2048, 9),
     (300, 1, 16, 33, 10),
+    (20, 4, 1024, 1000, 11),   # R = 100, the many-row GEMM's pipelined path, ragged V
+    (30, 4, 512, 2050, 12),    # R = 150: two row tiles, shortest pipelined d, V % 4 != 0
 ]
 
 
