@@ -40,14 +40,12 @@ sys.path.insert(0, ROOT)
 
 import perfmodel  # noqa: E402
 
-COUNTERS = os.path.join(ROOT, "profiles", "lmhead_gemma_e2b_counters.json")
-KERNEL_SOURCES = ["draft_token_verification_02_amd/csrc/lmhead.hip",
-                  "draft_token_verification_02_amd/csrc/sv_common.h"]
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_hash() -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in files:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -56,16 +54,21 @@ def kernel_hash() -> str:
 def traffic_from_counters(cfg_name: str):
     """HBM bytes per LM-head launch from committed rocprofv3 counter runs.
 
-    None when there is no summary for this workload or the kernel source has
-    changed since the counters were taken.
+    The summaries (profiles/*_counters.json) were taken with the default mode
+    (dense q) of one workload each; each records a hash of its kernel's
+    sources.  None when there is no summary for this workload or the kernel
+    source has changed since the counters were taken.
     """
-    if not os.path.exists(COUNTERS):
-        return None
-    with open(COUNTERS) as f:
-        c = json.load(f)
-    if c.get("workload") != cfg_name or c.get("kernel_hash") != kernel_hash():
-        return None
-    return c.get("hbm_bytes_per_launch")
+    import glob
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_counters.json"))):
+        with open(path) as f:
+            c = json.load(f)
+        if c.get("workload") != cfg_name:
+            continue
+        if c.get("kernel_hash") != source_hash(c.get("kernel_sources", [])):
+            return None
+        return c.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(x: dict, budget_s: float = 20.0, greedy: bool = False) -> dict:
@@ -280,11 +283,12 @@ def main():
         else:
             step_bytes = perfmodel.step_bytes(B, g, d, V, int((n_host < g).sum()))
         # R <= 64 rows: the streaming kernel, one launch per 64 rows; more
-        # rows: the LDS-tiled GEMM in one launch (when its partials fit, as in
-        # every named workload).
+        # rows: one launch of the pipelined 128-row GEMM (R <= 128) or of the
+        # 256 x 256 LDS-tiled GEMM (when their partials fit, as in every named
+        # workload).
         tiled = R > 64 and -(-V // 256) <= 1024
         passes = 1 if tiled else -(-R // 64)
-        kernel = "lmhead_tiled_kernel" if tiled else "lmhead_kernel"
+        kernel = ("lmhead_mid_kernel" if R <= 128 else "lmhead_big_kernel") if tiled else "lmhead_kernel"
         if mode == "greedy":
             kernel += " + greedy_kernel"
     # Bound by whichever roofline takes longer for the algorithmic work.
@@ -298,7 +302,7 @@ def main():
         roof = {"bound": "hbm", "kernel": kernel, "achieved": lm_bytes / lm_avg_s / 1e9,
                 "peak": perfmodel.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] * 1e9 / perfmodel.MI355X_HBM_BYTES_PER_S
-    roof["traffic"] = None if mode in ("greedy", "head") or tiled else traffic_from_counters(cfg.name)
+    roof["traffic"] = traffic_from_counters(cfg.name) if mode == "sample" else None
     roof["alg_bytes_per_launch"] = lm_bytes // passes
     roof["hbm_GBps_alg"] = lm_bytes / lm_avg_s / 1e9
 
