@@ -276,7 +276,7 @@ constexpr int tail_wait(int h) {
 }
 
 template <int FV, int FR, int WV, int WR, int U, bool FAST>
-__global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
+__global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
     float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
@@ -284,9 +284,11 @@ __global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
     constexpr int TR = kLmTile * FR * WR;             // rows per workgroup
     constexpr int kWaveV = kLmTile * FV;
     constexpr int kWaveR = kLmTile * FR;
-    constexpr int CH = TR * (kTK / 8) / kTThreads;    // 16-byte hidden chunks per thread per tile
-    static_assert(WV * WR == 4 && kWaveV * WV == kTV, "wave grid");
-    static_assert(!FAST || ((U == 4 || U == 8) && FR % 8 == 0), "ring depth and fragment groups");
+    constexpr int NW = WV * WR;                       // waves
+    constexpr int NT = NW * kWave;                    // threads
+    constexpr int CH = TR * (kTK / 8) / NT;           // 16-byte hidden chunks per thread per tile
+    static_assert(kWaveV * WV == kTV && CH >= 1, "wave grid");
+    static_assert(!FAST || ((U == 2 || U == 4 || U == 8) && FR % 8 == 0), "ring depth and fragment groups");
 
     // FAST: four stages of TR x 128 bytes (swizzled), each its own array so
     // that the compiler can tell a stage being read from the stages the
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
     auto load_b = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const int c = threadIdx.x + j * kTThreads;
+            const int c = threadIdx.x + j * NT;
             const int row = c >> 3, col = (c & 7) * 8;
             const int r = min(r0 + row, R - 1);          // pad rows repeat the last row
             if (FAST || k0 + col < d) hb[j] = *reinterpret_cast<const u32x4*>(hidden + (size_t)r * d + k0 + col);
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
     auto store_b = [&](char* l) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const int c = threadIdx.x + j * kTThreads;
+            const int c = threadIdx.x + j * NT;
             const int row = c >> 3, col = c & 7;
             *reinterpret_cast<u32x4*>(l + row * kRowBytes + col * 16) = hb[j];
         }
@@ -396,12 +398,12 @@ __global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
         // makes every wave's part visible.  The loop body covers kStages
         // tiles, so stages and ring slots are compile-time constants.
         constexpr int S = kStages;
-        constexpr int CHD = TR * 8 / kTThreads;            // copies per thread per tile
+        constexpr int CHD = TR * 8 / NT;                   // copies per thread per tile
         auto stage = [&](int st) { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
         auto copy_b = [&](int kt, int st) {
 #pragma unroll
             for (int j = 0; j < CHD; ++j) {
-                const int blk = j * 4 + wave;                // 1 KB block of the stage
+                const int blk = j * NW + wave;               // 1 KB block of the stage
                 const int c = blk * kWave + lane;
                 const int row = c >> 3, g = (c & 7) ^ (row & 7);
                 const int r = min(r0 + row, R - 1);          // pad rows repeat the last row
@@ -415,17 +417,18 @@ __global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
         const int off0 = ((0 * 4 + kg) ^ (r16 & 7)) * 16, off1 = ((1 * 4 + kg) ^ (r16 & 7)) * 16;
         auto step_dma = [&](int st, int s, int slot) {
             const char* lh = stage(st) + brow + (s ? off1 : off0);
-            // B fragments eight at a time (register budget), each used by all FV
+            // B fragments kFB at a time (register budget), each used by all FV
+            constexpr int kFB = 8;
 #pragma unroll
-            for (int b0 = 0; b0 < FR; b0 += 8) {
-                u32x4 fb[8];
+            for (int b0 = 0; b0 < FR; b0 += kFB) {
+                u32x4 fb[kFB];
 #pragma unroll
-                for (int b = 0; b < 8; ++b)
+                for (int b = 0; b < kFB; ++b)
                     fb[b] = *reinterpret_cast<const u32x4*>(lh + (b0 + b) * kLmTile * 128);
 #pragma unroll
                 for (int a = 0; a < FV; ++a)
 #pragma unroll
-                    for (int b = 0; b < 8; ++b)
+                    for (int b = 0; b < kFB; ++b)
                         acc[a][b0 + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(bf16x8, ar[slot][a]), __builtin_bit_cast(bf16x8, fb[b]),
                             acc[a][b0 + b], 0, 0, 0);
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(kTThreads) void lmhead_mid_kernel(
         if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; s_av[wv][rl] = av; s_ai[wv][rl] = ai; }
     }
     __syncthreads();
-    for (int rl = threadIdx.x; rl < TR; rl += kTThreads) {
+    for (int rl = threadIdx.x; rl < TR; rl += NT) {
         if (r0 + rl >= R) break;
         float m = -INFINITY, s = 0.f, av = -INFINITY;
         int ai = -1;
@@ -572,11 +575,11 @@ hipError_t launch_shape(const uint16_t* hidden, const uint16_t* W, int R, int d,
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
     // pipelined: d a multiple of 4 tiles of 64, at least two groups of them
     if (d % (kTK * kStages) == 0 && d / (kTK * kStages) >= 2)
-        lmhead_mid_kernel<FV, FR, WV, WR, U, true><<<dim3(grid), dim3(kTThreads), 0, stream>>>(
+        lmhead_mid_kernel<FV, FR, WV, WR, U, true><<<dim3(grid), dim3(WV * WR * kWave), 0, stream>>>(
             hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
             n_counters);
     else
-        lmhead_mid_kernel<FV, FR, WV, WR, 2, false><<<dim3(grid), dim3(kTThreads), 0, stream>>>(
+        lmhead_mid_kernel<FV, FR, WV, WR, 2, false><<<dim3(grid), dim3(WV * WR * kWave), 0, stream>>>(
             hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
             n_counters);
     return hipGetLastError();
