@@ -10,15 +10,16 @@
 // Four launches, N hidden rows (one per drafted position):
 //   scores_kernel  cluster logits h . centroid^T, [N][C] fp32.  The table is
 //                  small (C x d bf16, 6 MB at C = 2048, d = 1536), so each
-//                  workgroup takes 16 centroids and splits k over its waves
-//                  (v_mfma_f32_16x16x32_bf16, centroids as A, hidden rows as
-//                  B), summed through LDS in wave order: C / 16 workgroups
-//                  all streaming at once instead of a few long ones.
+//                  workgroup takes 16 centroids and splits k over its eight
+//                  waves (v_mfma_f32_16x16x32_bf16, centroids as A, hidden
+//                  rows as B), each issuing its k steps' loads together, and
+//                  sums them through LDS in wave order: C / 16 workgroups of
+//                  one memory round trip each instead of a few long ones.
 //   topk_kernel    per row, the k largest cluster logits (ties to the lower
 //                  cluster id) by an exact 4-pass radix select on order-
-//                  preserving keys, then the chosen clusters in ascending id
-//                  and their members in the members table's order: the
-//                  row's K = k * M token ids.
+//                  preserving keys (two barriers per pass), then the chosen
+//                  clusters in ascending id and their members in the members
+//                  table's order: the row's K = k * M token ids.
 //   gather_kernel  token logits h . W[id] for the K ids of each row: W rows
 //                  gathered straight into the MFMA A operand (16 tokens per
 //                  fragment, 16 contiguous bytes per lane), the hidden row as
@@ -33,16 +34,21 @@ namespace sv {
 
 namespace {
 
-constexpr int kSplit = 4;            // waves splitting k in scores_kernel
+constexpr int kSplit = 8;            // waves splitting k in scores_kernel
 constexpr int kGT = 2;               // 16-token fragments per wave in gather_kernel
 constexpr int kGWaves = 4;           // waves per gather workgroup
 constexpr int kGU = 8;               // k-steps loaded per batch in gather_kernel
 
 // ---------------------------------------------------------------------------
+// Cluster logits for 16 centroids x 16 * MT hidden rows per workgroup; kSplit
+// waves take every kSplit-th 32-wide k step and issue up to kSB steps' loads
+// at once (at d = 1536 all of them: one memory round trip per wave), then the
+// waves' sums are added in wave order through LDS.
 template <int MT>
 __global__ __launch_bounds__(kSplit * kWave) void scores_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ cent, int N, int d, int C,
     float* __restrict__ scores) {
+    constexpr int kSB = 8;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r16 = lane & 15, kg = lane >> 4;
@@ -58,17 +64,25 @@ __global__ __launch_bounds__(kSplit * kWave) void scores_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nstep = (d + 31) / 32;
-#pragma unroll 4
-    for (int ks = wave; ks < nstep; ks += kSplit) {
-        const bool ok = ks * 32 + kg * 8 < d;          // d is a multiple of 8
-        const u32x4 zero{0u, 0u, 0u, 0u};
-        const u32x4 a = ok ? *reinterpret_cast<const u32x4*>(ap + ks * 32) : zero;
+    const u32x4 zero{0u, 0u, 0u, 0u};
+    for (int ks0 = wave; ks0 < nstep; ks0 += kSplit * kSB) {
+        u32x4 a[kSB], bb[kSB][MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const u32x4 b = ok ? *reinterpret_cast<const u32x4*>(bp[m] + ks * 32) : zero;
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[m], 0, 0, 0);
+        for (int u = 0; u < kSB; ++u) {
+            const int ks = ks0 + u * kSplit;
+            const bool ok = ks < nstep && ks * 32 + kg * 8 < d;    // d is a multiple of 8
+            a[u] = ok ? *reinterpret_cast<const u32x4*>(ap + ks * 32) : zero;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                bb[u][m] = ok ? *reinterpret_cast<const u32x4*>(bp[m] + ks * 32) : zero;
         }
+#pragma unroll
+        for (int u = 0; u < kSB; ++u)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, bb[u][m]), acc[m],
+                    0, 0, 0);
     }
 
     __shared__ f32x4 red[kSplit][MT][kWave];
@@ -78,15 +92,15 @@ __global__ __launch_bounds__(kSplit * kWave) void scores_kernel(
     if (wave == 0) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            f32x4 s = red[0][m][lane];
+            f32x4 sum = red[0][m][lane];
 #pragma unroll
-            for (int w = 1; w < kSplit; ++w) s += red[w][m][lane];
+            for (int w = 1; w < kSplit; ++w) sum += red[w][m][lane];
             // lane holds D[centroid 4*kg + i][hidden row r16] of fragment m
             const int n = n0 + m * kLmTile + r16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = c0 + 4 * kg + i;
-                if (n < N && c < C) scores[(size_t)n * C + c] = s[i];
+                if (n < N && c < C) scores[(size_t)n * C + c] = sum[i];
             }
         }
     }
@@ -134,73 +148,124 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(
     int V, int32_t* __restrict__ q_ids, int32_t* __restrict__ clusters) {
     __shared__ unsigned s_key[SV_HEAD_MAX_CLUSTERS];
     __shared__ int s_sel[SV_HEAD_MAX_CLUSTERS];
-    __shared__ int s_hist[256];
+    __shared__ int s_hist[2][kBlock / kWave][256];   // per wave: scores of one size share their top digits
     __shared__ int s_digit, s_above;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
     const int n = blockIdx.x;
     const float* row = scores + (size_t)n * C;
-    for (int c = tid; c < C; c += kBlock) {
-        s_key[c] = order_key(row[c]);
-        s_sel[c] = -1;
+    // Loads issued in batches of 8 per thread (one memory round trip each)
+    for (int c0 = 0; c0 < C; c0 += 8 * kBlock) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + tid + u * kBlock;
+            v[u] = c < C ? row[c] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = c0 + tid + u * kBlock;
+            if (c < C) { s_key[c] = order_key(v[u]); s_sel[c] = -1; }
+        }
     }
+    const int wave = tid / kWave;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) s_hist[0][w][tid] = 0;
+    __syncthreads();
 
     // The k-th largest key, 8 bits at a time from the top: at each pass count
     // the keys that match the digits found so far by their next digit, and
     // take the digit where the count of keys at or above it reaches the
-    // number still needed.
+    // number still needed.  The histograms alternate between two buffers (the
+    // next one is cleared during the pass), and one wave finds the digit:
+    // two barriers per pass.
     unsigned prefix = 0u, pmask = 0u;
     int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        s_hist[tid] = 0;
-        __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        int (*hist)[256] = s_hist[pass & 1];
         for (int c = tid; c < C; c += kBlock) {
             const unsigned key = s_key[c];
-            if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+            if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1);
         }
+#pragma unroll
+        for (int w = 0; w < kBlock / kWave; ++w) s_hist[(pass + 1) & 1][w][tid] = 0;
         __syncthreads();
-        const int v = s_hist[255 - tid];             // digits from the top
-        int total;
-        const int at_or_above = block_inclusive_scan_int(v, &total);
-        if (at_or_above >= need && at_or_above - v < need) {
-            s_digit = 255 - tid;
-            s_above = at_or_above - v;
+        if (tid < kWave) {
+            // lane l holds digits 255 - 4l .. 252 - 4l, highest first
+            int cnt[4], tot = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cnt[i] = 0;
+#pragma unroll
+                for (int w = 0; w < kBlock / kWave; ++w) cnt[i] += hist[w][255 - 4 * lane - i];
+                tot += cnt[i];
+            }
+            int incl = tot;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            const int before = incl - tot;               // keys with a higher digit
+            if (before < need && incl >= need) {
+                int run = before;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (run + cnt[i] >= need) { s_digit = 255 - 4 * lane - i; s_above = run; break; }
+                    run += cnt[i];
+                }
+            }
         }
         __syncthreads();
         prefix |= (unsigned)s_digit << shift;
         pmask |= 255u << shift;
         need -= s_above;
-        __syncthreads();
     }
     // Chosen: every key above the threshold, and the first `need` keys equal
-    // to it in cluster order.  Thread t owns clusters [t*per, (t+1)*per).
+    // to it in cluster order.  Thread t owns clusters [t*per, (t+1)*per); one
+    // scan of (count above, count equal) packed in 16-bit halves places them.
     const int per = (C + kBlock - 1) / kBlock;
     const int cb = tid * per, ce = min(C, cb + per);
-    int neq = 0;
-    for (int c = cb; c < ce; ++c) neq += s_key[c] == prefix;
-    const int eq_before = block_exclusive_scan_int(neq);
-    auto chosen = [&](int c, int& eqs) {
+    int ngt = 0, neq = 0;
+    for (int c = cb; c < ce; ++c) {
         const unsigned key = s_key[c];
-        if (key > prefix) return true;
-        if (key == prefix) return eqs++ < need;
-        return false;
-    };
-    int nsel = 0, eqs = eq_before;
-    for (int c = cb; c < ce; ++c) nsel += chosen(c, eqs);
-    int pos = block_exclusive_scan_int(nsel);
-    eqs = eq_before;
-    for (int c = cb; c < ce; ++c)
-        if (chosen(c, eqs)) s_sel[pos++] = c;
+        ngt += key > prefix;
+        neq += key == prefix;
+    }
+    const int packed = block_exclusive_scan_int((ngt << 16) | neq);
+    const int gt_before = packed >> 16, eq_before = packed & 0xffff;
+    int pos = gt_before + min(eq_before, need), eqs = eq_before;
+    for (int c = cb; c < ce; ++c) {
+        const unsigned key = s_key[c];
+        const bool chosen = key > prefix || (key == prefix && eqs++ < need);
+        if (chosen) s_sel[pos++] = c;
+    }
     __syncthreads();
 
     if (clusters)
         for (int j = tid; j < k; j += kBlock) clusters[(size_t)n * k + j] = s_sel[j];
     const int K = k * M;
     int32_t* out = q_ids + (size_t)n * K;
-    for (int e = tid; e < K; e += kBlock) {
-        const int j = e / M, m = e - j * M;
-        const int c = s_sel[j];                 // always a chosen cluster; -1 never read
-        const int id = c >= 0 ? members[(size_t)c * M + m] : -1;
-        out[e] = id >= 0 && id < V ? id : -1;
+    // The members of the chosen clusters, gathered 8 per thread at a time.
+    for (int e0 = 0; e0 < K; e0 += 8 * kBlock) {
+        int id[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + tid + u * kBlock;
+            id[u] = -1;
+            if (e < K) {
+                const int j = e / M, m = e - j * M;
+                const int c = s_sel[j];         // always a chosen cluster; -1 never read
+                if (c >= 0) id[u] = members[(size_t)c * M + m];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + tid + u * kBlock;
+            if (e < K) out[e] = id[u] >= 0 && id[u] < V ? id[u] : -1;
+        }
     }
 }
 
@@ -317,10 +382,17 @@ __global__ __launch_bounds__(kBlock) void qfinal_kernel(
     }
     __syncthreads();
     const float m = s_m, s = s_s;
-    const int j1 = min(K, (int)(blockIdx.x + 1) * kBlock * kQPer);
-    for (int j = blockIdx.x * kBlock * kQPer + threadIdx.x; j < j1; j += kBlock) {
-        const float l = tl[(size_t)n * K + j];
-        q_vals[(size_t)n * K + j] = s > 0.f && l != -INFINITY ? expf(l - m) / s : 0.f;
+    const int jb = blockIdx.x * kBlock * kQPer + threadIdx.x;
+    float l[kQPer];
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+        const int j = jb + u * kBlock;
+        l[u] = j < K ? tl[(size_t)n * K + j] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+        const int j = jb + u * kBlock;
+        if (j < K) q_vals[(size_t)n * K + j] = s > 0.f && l[u] != -INFINITY ? expf(l[u] - m) / s : 0.f;
     }
 }
 
