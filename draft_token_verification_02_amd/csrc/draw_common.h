@@ -15,10 +15,6 @@ namespace sv {
 
 namespace {
 
-constexpr int kRowThreads = 32;                  // threads merging one row's partials
-constexpr int kRowsPerPass = kBlock / kRowThreads;
-constexpr int kMergeLoads = 2;                   // float4 loads per thread per row and batch
-
 __device__ __forceinline__ float target_prob(float logit, float row_max, float row_sum) {
     return expf(logit - row_max) / row_sum;
 }
@@ -95,37 +91,41 @@ __device__ __forceinline__ int block_min_int(int v) {
 __device__ __forceinline__ int block_max_int(int v) { return -block_min_int(-v); }
 
 // Softmax normalisers (max, sum exp) of rows row0 .. row0+nrows-1 from the
-// LM-head's per-workgroup partials, into r_m[i], r_s[i].  Every thread of the
-// workgroup takes part; the caller synchronises before reading the results.
-__device__ void merge_row_partials(const float* __restrict__ part_max,
-                                   const float* __restrict__ part_sum, int NP, int NPs, size_t row0,
-                                   int nrows, float* r_m, float* r_s) {
-    // 32 threads per row, 8 rows per pass.  A batch is kMergeLoads float4 of
-    // maxima and of sums per thread (256 partials per row), loaded before
-    // use; the persistent LM-head grid (one workgroup per CU) fits in one.
-    const int sub = threadIdx.x % kRowThreads;
-    const int grp = threadIdx.x / kRowThreads;
+// LM-head's per-workgroup partials, into r_m[i], r_s[i].  TPR threads of one
+// wave share a row (TPR = 32, 16 or 8, the most that still fits every row in
+// one pass when it can), each loading its 16-byte groups of maxima and sums
+// kBatch at a time before merging them, so a row costs one memory round trip
+// per kBatch * TPR * 4 partials.  Every thread of the workgroup takes part;
+// the caller synchronises before reading the results.
+template <int TPR>
+__device__ void merge_row_partials_t(const float* __restrict__ part_max,
+                                     const float* __restrict__ part_sum, int NP, int NPs,
+                                     size_t row0, int nrows, float* r_m, float* r_s) {
+    constexpr int kRows = kBlock / TPR;          // rows per pass
+    constexpr int kBatch = 8;                    // float4 loads per thread and array in flight
+    const int sub = threadIdx.x % TPR;
+    const int grp = threadIdx.x / TPR;
     const int n4 = (NP + 3) / 4;
-    for (int i0 = 0; i0 < nrows; i0 += kRowsPerPass) {
+    for (int i0 = 0; i0 < nrows; i0 += kRows) {
         const int i = i0 + grp;
         float m = -INFINITY, s = 0.f;
         if (i < nrows) {
             const size_t r = row0 + i;
             const float4* pm = reinterpret_cast<const float4*>(part_max + r * NPs);
             const float4* ps = reinterpret_cast<const float4*>(part_sum + r * NPs);
-            for (int j0 = 0; j0 < n4; j0 += kMergeLoads * kRowThreads) {
-                float4 a[kMergeLoads], c[kMergeLoads];
+            for (int j0 = 0; j0 < n4; j0 += kBatch * TPR) {
+                float4 a[kBatch], c[kBatch];
 #pragma unroll
-                for (int u = 0; u < kMergeLoads; ++u) {
-                    const int jj = j0 + sub + u * kRowThreads;
+                for (int u = 0; u < kBatch; ++u) {
+                    const int jj = j0 + sub + u * TPR;
                     a[u] = jj < n4 ? pm[jj] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
                     c[u] = jj < n4 ? ps[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
                 // this batch's max, then its rescaled sum, merged into (m, s)
                 float bm = -INFINITY, bs = 0.f;
 #pragma unroll
-                for (int u = 0; u < kMergeLoads; ++u) {
-                    const int j = 4 * (j0 + sub + u * kRowThreads);   // entries past NP are padding
+                for (int u = 0; u < kBatch; ++u) {
+                    const int j = 4 * (j0 + sub + u * TPR);      // entries past NP are padding
                     if (j + 0 < NP) bm = fmaxf(bm, a[u].x);
                     if (j + 1 < NP) bm = fmaxf(bm, a[u].y);
                     if (j + 2 < NP) bm = fmaxf(bm, a[u].z);
@@ -133,8 +133,8 @@ __device__ void merge_row_partials(const float* __restrict__ part_max,
                 }
                 if (bm != -INFINITY) {
 #pragma unroll
-                    for (int u = 0; u < kMergeLoads; ++u) {
-                        const int j = 4 * (j0 + sub + u * kRowThreads);
+                    for (int u = 0; u < kBatch; ++u) {
+                        const int j = 4 * (j0 + sub + u * TPR);
                         if (j + 0 < NP && a[u].x != -INFINITY) bs += c[u].x * expf(a[u].x - bm);
                         if (j + 1 < NP && a[u].y != -INFINITY) bs += c[u].y * expf(a[u].y - bm);
                         if (j + 2 < NP && a[u].z != -INFINITY) bs += c[u].z * expf(a[u].z - bm);
@@ -145,12 +145,23 @@ __device__ void merge_row_partials(const float* __restrict__ part_max,
             }
         }
 #pragma unroll
-        for (int off = 1; off < kRowThreads; off <<= 1) {
+        for (int off = 1; off < TPR; off <<= 1) {
             const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
             lse_merge(m, s, m2, s2);
         }
         if (sub == 0 && i < nrows) { r_m[i] = m; r_s[i] = s; }
     }
+}
+
+__device__ void merge_row_partials(const float* __restrict__ part_max,
+                                   const float* __restrict__ part_sum, int NP, int NPs, size_t row0,
+                                   int nrows, float* r_m, float* r_s) {
+    if (nrows <= kBlock / 32)
+        merge_row_partials_t<32>(part_max, part_sum, NP, NPs, row0, nrows, r_m, r_s);
+    else if (nrows <= kBlock / 16)
+        merge_row_partials_t<16>(part_max, part_sum, NP, NPs, row0, nrows, r_m, r_s);
+    else
+        merge_row_partials_t<8>(part_max, part_sum, NP, NPs, row0, nrows, r_m, r_s);
 }
 
 // ---------------------------------------------------------------------------

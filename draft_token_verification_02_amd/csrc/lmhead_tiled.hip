@@ -135,13 +135,16 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
         for (int b = 0; b < kFR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (d + kTK - 1) / kTK;
+    // K tiles from an offset of the block's own (see lmhead_mid_kernel).
+    const int rot = (int)(((unsigned)vb * 2654435761u >> 16) % (unsigned)nk);
+    auto ktile = [&](int kt) { const int t = kt + rot; return (t >= nk ? t - nk : t) * kTK; };
     BigStage st;
-    big_load_stage(st, W, hidden, v0, r0, 0, V, R, d);
+    big_load_stage(st, W, hidden, v0, r0, ktile(0), V, R, d);
     big_store_stage(st, lds[0][0], lds[0][1]);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) big_load_stage(st, W, hidden, v0, r0, (kt + 1) * kTK, V, R, d);
+        if (kt + 1 < nk) big_load_stage(st, W, hidden, v0, r0, ktile(kt + 1), V, R, d);
         const char* lw = lds[cur][0] + (wv * kWaveV + r16) * kRowBytes + kg * 16;
         const char* lh = lds[cur][1] + (wr * kWaveR + r16) * kRowBytes + kg * 16;
 #pragma unroll
@@ -330,10 +333,21 @@ __global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
     const int nsteps = (d + 31) / 32;
     const u32x4 zero{0u, 0u, 0u, 0u};
     u32x4 ar[U][FV];
+    // The pipelined path walks k from a tile offset of its own (a hash of the
+    // vocab block), wrapping: k is a pure reduction, so only the fp32
+    // summation order changes, and the workgroups in flight no longer all
+    // read the same offset within their rows at once (which made the time
+    // depend on where the allocation of W sat in HBM).
+    const int nk_all = (d + kTK - 1) / kTK;
+    const int rot = FAST ? (int)(((unsigned)vb * 2654435761u >> 16) % (unsigned)nk_all) : 0;
+    auto kstep = [&](int ks) {               // rotated 32-wide k step
+        const int k = ks + 2 * rot;
+        return k >= nsteps ? k - nsteps : k;
+    };
     auto load_a = [&](int slot, int ks) {
 #pragma unroll
         for (int a = 0; a < FV; ++a) {
-            if (FAST) ar[slot][a] = *reinterpret_cast<const u32x4*>(ap[a] + ks * 32);
+            if (FAST) ar[slot][a] = *reinterpret_cast<const u32x4*>(ap[a] + kstep(ks) * 32);
             else ar[slot][a] = ks * 32 + kg * 8 < d ? *reinterpret_cast<const u32x4*>(ap[a] + ks * 32)
                                                     : zero;
         }
@@ -408,7 +422,7 @@ __global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
                 const int row = c >> 3, g = (c & 7) ^ (row & 7);
                 const int r = min(r0 + row, R - 1);          // pad rows repeat the last row
                 __builtin_amdgcn_global_load_lds(
-                    hidden + (size_t)r * d + kt * kTK + g * 8,
+                    hidden + (size_t)r * d + (kt + rot < nk ? kt + rot : kt + rot - nk) * kTK + g * 8,
                     (__attribute__((address_space(3))) void*)(stage(st) + blk * 1024), 16, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
