@@ -8,11 +8,11 @@
 //     later drafts; when every draft passes, emit the target's own token at
 //     the extra position, which the same weight read already scored.
 //
-// After the LM head, one 256-thread workgroup per (sequence b, 4096-token
-// chunk c) of draw_kernel.  For sequence b they
+// After the LM head, one 1024-thread workgroup per (sequence b, 4096-token
+// chunk c) of draw_kernel, four tokens per thread.  For sequence b they
 //   1. gather l[x_i], q[x_i] and r_i of the gamma drafts and, meanwhile,
-//      merge each of the sequence's gamma+1 rows' LM-head partials (16-byte
-//      loads, 32 threads per row) into the row's softmax normaliser;
+//      merge each of the sequence's gamma+1 rows' LM-head partials (one
+//      wave per row) into the row's softmax normaliser;
 //   2. run the gamma accept tests r * q <= p and take n, the number of
 //      leading accepts, from a wave ballot;
 //   3. compute fp64 totals of the chunk's draw weights -- the residual
@@ -89,16 +89,16 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
             const int K4 = q.K >> 2;
             const int total = gamma * K4;
             const int4* id4 = reinterpret_cast<const int4*>(ids);
-            for (int e0 = 0; e0 < total; e0 += kBlock * 8) {
+            for (int e0 = 0; e0 < total; e0 += kDrawBlock * 8) {
                 int4 v[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int e = e0 + threadIdx.x + u * kBlock;
+                    const int e = e0 + threadIdx.x + u * kDrawBlock;
                     v[u] = e < total ? id4[e] : make_int4(-1, -1, -1, -1);
                 }
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int e = e0 + threadIdx.x + u * kBlock;
+                    const int e = e0 + threadIdx.x + u * kDrawBlock;
                     if (e >= total) continue;
                     const int i = e / K4;
                     const int x = s_x[i];
@@ -113,7 +113,7 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
             }
         } else {
             const int total = gamma * q.K;
-            for (int e = threadIdx.x; e < total; e += kBlock) {
+            for (int e = threadIdx.x; e < total; e += kDrawBlock) {
                 const int id = ids[e];
                 const int i = e / q.K;
                 badq |= id >= V;
@@ -146,7 +146,7 @@ __device__ int accept_tests(const float* __restrict__ logits, const float* __res
 // Accept tests once per sequence (the split form, for many sequences):
 // n, the row normalisers, the kept drafts, padding and status.
 template <bool SPARSE>
-__global__ __launch_bounds__(kBlock) void accept_kernel(
+__global__ __launch_bounds__(kDrawBlock) void accept_kernel(
     const float* __restrict__ logits, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
     QArg q, const float* __restrict__ uniforms, int gamma, int V,
@@ -176,16 +176,15 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(
 // row's normaliser it left, only writes its chunk totals, and pick_kernel
 // follows: the kernel boundary orders the totals before the pick.
 template <bool FUSED, bool SPARSE>
-__global__ __launch_bounds__(kBlock) void draw_kernel(
+__global__ __launch_bounds__(kDrawBlock) void draw_kernel(
     const float* __restrict__ logits, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
-    QArg q, const float* __restrict__ uniforms, int gamma, int V, int NC,
-    double* __restrict__ csum, double* __restrict__ psum, int32_t* __restrict__ counters,
-    float* __restrict__ row_max, float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
+    QArg q, const float* __restrict__ uniforms, int gamma, int V, int NC, ChunkSums cs,
+    int32_t* __restrict__ counters, float* __restrict__ row_max, float* __restrict__ row_sum,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_accepted,
+    int32_t* __restrict__ status) {
     __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
     __shared__ __attribute__((aligned(16))) unsigned s_qc[SPARSE ? kDrawChunk : 4];
-    __shared__ int s_last;
     // flat grid: workgroup x covers chunk x % NC of sequence x / NC
     const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
     const int g1 = gamma + 1;
@@ -204,29 +203,18 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
         S = row_sum[(size_t)b * g1 + n];
     }
     const DrawRow d = draw_row<SPARSE>(logits, q, b, gamma, n, V, M, S);
-    const int cs = c * kDrawChunk;
-    if (SPARSE && d.has_q()) stage_sparse_chunk(d, cs, s_qc);
+    const int c0 = c * kDrawChunk;
+    if (SPARSE && d.has_q()) stage_sparse_chunk(d, c0, s_qc);
 
     float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights16<SPARSE>(d, cs + threadIdx.x * kDrawPerThread, s_qc, cs, w, p);
+    draw_weights<SPARSE>(d, c0 + threadIdx.x * kDrawPerThread, s_qc, c0, w, p);
     double tw = 0.0, tp = 0.0;
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
-    double tot_w, tot_p;
-    block_inclusive_scan(tw, &tot_w);
-    block_inclusive_scan(tp, &tot_p);
-    if (threadIdx.x == 0) {
-        csum[(size_t)b * NC + c] = tot_w;
-        psum[(size_t)b * NC + c] = tot_p;
-        if (FUSED) {
-            __threadfence();                   // publish the totals before counting
-            s_last = atomicAdd(&counters[b], 1) == NC - 1;
-        }
-    }
+    store_chunk_totals(tw, tp, cs, (size_t)b * NC + c);
     if (!FUSED) return;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();                           // see every other chunk's totals
+    if (!arrive_last(&counters[b], NC)) return;
+    if (threadIdx.x >= kWave) return;          // the rest is one wave's
 
     // The sequence's last workgroup: outputs that depend on n only ...
     if (FUSED && threadIdx.x < g1) {
@@ -235,9 +223,9 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
         row_sum[(size_t)b * g1 + i] = r_s[i];
         if (i != n) out_tokens[(size_t)b * g1 + i] = i < n ? draft[(size_t)b * gamma + i] : -1;
     }
-    // ... and the draw.
+    // ... and the draw (the chunk pass is done with s_qc).
     int pflags;
-    const int tok = pick<SPARSE>(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], s_qc, &pflags);
+    const int tok = pick<SPARSE>(d, b, NC, cs, uniforms[(size_t)b * g1 + gamma], s_qc, &pflags);
     if (threadIdx.x == 0) {
         out_tokens[(size_t)b * g1 + n] = tok;
         n_accepted[b] = n;
@@ -246,22 +234,23 @@ __global__ __launch_bounds__(kBlock) void draw_kernel(
     }
 }
 
-// The draw for one sequence from the chunk totals draw_kernel<false> wrote.
+// The draw for one sequence from the chunk totals draw_kernel<false> wrote:
+// one wave per sequence.
 template <bool SPARSE>
-__global__ __launch_bounds__(kBlock) void pick_kernel(
+__global__ __launch_bounds__(kWave) void pick_kernel(
     const float* __restrict__ logits, QArg q,
-    const float* __restrict__ uniforms, int gamma, int V, int NC, const double* __restrict__ csum,
-    const double* __restrict__ psum, const float* __restrict__ row_max,
-    const float* __restrict__ row_sum, int32_t* __restrict__ out_tokens,
-    const int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
-    __shared__ __attribute__((aligned(16))) unsigned s_qc[SPARSE ? kDrawChunk : 4];
+    const float* __restrict__ uniforms, int gamma, int V, int NC, ChunkSums cs,
+    const float* __restrict__ row_max, const float* __restrict__ row_sum,
+    int32_t* __restrict__ out_tokens, const int32_t* __restrict__ n_accepted,
+    int32_t* __restrict__ status) {
+    __shared__ __attribute__((aligned(16))) unsigned s_qc[SPARSE ? kWave * kDrawPerThread : 4];
     const int b = blockIdx.x;
     const int g1 = gamma + 1;
     const int n = n_accepted[b];
     const size_t k = (size_t)b * g1 + n;
     const DrawRow d = draw_row<SPARSE>(logits, q, b, gamma, n, V, row_max[k], row_sum[k]);
     int flags;
-    const int tok = pick<SPARSE>(d, b, NC, csum, psum, uniforms[(size_t)b * g1 + gamma], s_qc, &flags);
+    const int tok = pick<SPARSE>(d, b, NC, cs, uniforms[(size_t)b * g1 + gamma], s_qc, &flags);
     if (threadIdx.x == 0) {
         out_tokens[k] = tok;
         if (flags) status[b] |= flags;
@@ -279,7 +268,7 @@ namespace {
 template <bool SPARSE>
 hipError_t launch_accept_draw_t(const float* logits, const float* part_max, const float* part_sum,
                                 int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
-                                QArg q, const float* uniforms, int NC, double* csum, double* psum,
+                                QArg q, const float* uniforms, int NC, const ChunkSums& cs,
                                 int32_t* counters, float* row_max, float* row_sum,
                                 int32_t* out_tokens, int32_t* n_accepted, int32_t* status,
                                 hipStream_t stream) {
@@ -289,24 +278,24 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
     // then the pick -- three launches, no workgroup repeats the accept tests
     // and none waits on a device-wide fence.
     if (groups <= SV_FUSE_MAX_GROUPS) {
-        draw_kernel<true, SPARSE><<<dim3(groups), dim3(kBlock), 0, stream>>>(
-            logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum,
-            counters, row_max, row_sum, out_tokens, n_accepted, status);
+        draw_kernel<true, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+            logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
+            row_max, row_sum, out_tokens, n_accepted, status);
         return hipGetLastError();
     }
-    accept_kernel<SPARSE><<<dim3(B), dim3(kBlock), 0, stream>>>(
+    accept_kernel<SPARSE><<<dim3(B), dim3(kDrawBlock), 0, stream>>>(
         logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, row_max, row_sum,
         out_tokens, n_accepted, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    draw_kernel<false, SPARSE><<<dim3(groups), dim3(kBlock), 0, stream>>>(
-        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, csum, psum,
-        counters, row_max, row_sum, out_tokens, n_accepted, status);
+    draw_kernel<false, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
+        row_max, row_sum, out_tokens, n_accepted, status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    pick_kernel<SPARSE><<<dim3(B), dim3(kBlock), 0, stream>>>(logits, q, uniforms, gamma, V, NC,
-                                                             csum, psum, row_max, row_sum,
-                                                             out_tokens, n_accepted, status);
+    pick_kernel<SPARSE><<<dim3(B), dim3(kWave), 0, stream>>>(logits, q, uniforms, gamma, V, NC, cs,
+                                                            row_max, row_sum, out_tokens,
+                                                            n_accepted, status);
     return hipGetLastError();
 }
 
@@ -316,16 +305,16 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
 hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
                               int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
                               const float* q, const int32_t* q_idx, int K, const float* uniforms,
-                              int NC, double* csum, double* psum, int32_t* counters,
+                              int NC, const ChunkSums& cs, int32_t* counters,
                               float* row_max, float* row_sum, int32_t* out_tokens,
                               int32_t* n_accepted, int32_t* status, hipStream_t stream) {
     const QArg qa{q, q_idx, K};
     if (q_idx)
         return launch_accept_draw_t<true>(logits, part_max, part_sum, NP, NPs, B, gamma, V, draft,
-                                          qa, uniforms, NC, csum, psum, counters, row_max, row_sum,
+                                          qa, uniforms, NC, cs, counters, row_max, row_sum,
                                           out_tokens, n_accepted, status, stream);
     return launch_accept_draw_t<false>(logits, part_max, part_sum, NP, NPs, B, gamma, V, draft, qa,
-                                       uniforms, NC, csum, psum, counters, row_max, row_sum,
+                                       uniforms, NC, cs, counters, row_max, row_sum,
                                        out_tokens, n_accepted, status, stream);
 }
 

@@ -21,7 +21,7 @@ hipError_t launch_greedy(const float* part_max, const int32_t* part_arg, int NP,
 hipError_t launch_accept_draw(const float* logits, const float* part_max, const float* part_sum,
                               int NP, int NPs, int B, int gamma, int V, const int32_t* draft,
                               const float* q, const int32_t* q_idx, int K, const float* uniforms,
-                              int NC, double* csum, double* psum, int32_t* counters,
+                              int NC, const ChunkSums& cs, int32_t* counters,
                               float* row_max, float* row_sum, int32_t* out_tokens,
                               int32_t* n_accepted, int32_t* status, hipStream_t stream);
 hipError_t launch_sparse_head(const uint16_t* h, const uint16_t* W, const uint16_t* cent,
@@ -31,7 +31,7 @@ hipError_t launch_sparse_head(const uint16_t* h, const uint16_t* W, const uint16
 hipError_t launch_tree(const float* logits, const float* part_max, const float* part_sum, int NP,
                        int NPs, int B, int V, const TreeTopo& tp, int rounds,
                        const int32_t* tokens, const float* q, const float* uniforms, int NC,
-                       double* csum, double* psum, float* row_max, float* row_sum, void* state,
+                       const ChunkSums& cs, float* row_max, float* row_sum, void* state,
                        int32_t* counters, int32_t* out_tokens, int32_t* n_accepted,
                        int32_t* path_nodes, int32_t* status, hipStream_t stream);
 }  // namespace sv
@@ -93,6 +93,11 @@ sv_status stage2_greedy(const int32_t* draft, sv_dims dims, int32_t* out_tokens,
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
+sv::ChunkSums chunk_sums(void* ws, const sv::Layout& L) {
+    return {at<double>(ws, L.csum), at<double>(ws, L.psum), at<double>(ws, L.cwave),
+            at<double>(ws, L.pwave)};
+}
+
 // q_idx == nullptr: dense q [B][gamma][V]; otherwise sparse q with K entries per row.
 sv_status stage2(const int32_t* draft, const float* q, const int32_t* q_idx, int K,
                  const float* uniforms, sv_dims dims, int32_t* out_tokens, int32_t* n_accepted,
@@ -101,8 +106,8 @@ sv_status stage2(const int32_t* draft, const float* q, const int32_t* q_idx, int
     hipError_t e = sv::launch_accept_draw(
         at<float>(ws, L.logits), at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
         lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.gamma, dims.V, draft, q, q_idx, K,
-        uniforms, L.NC, at<double>(ws, L.csum), at<double>(ws, L.psum),
-        at<int32_t>(ws, L.counters), at<float>(ws, L.row_max), at<float>(ws, L.row_sum),
+        uniforms, L.NC, chunk_sums(ws, L), at<int32_t>(ws, L.counters),
+        at<float>(ws, L.row_max), at<float>(ws, L.row_sum),
         out_tokens, n_accepted, at<int32_t>(ws, L.status), s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
@@ -372,8 +377,8 @@ sv_status spec_verify_tree(const uint16_t* hidden, const uint16_t* W_lmhead, con
     const hipError_t e = sv::launch_tree(
         at<float>(workspace, L.logits), at<float>(workspace, L.part_max),
         at<float>(workspace, L.part_sum), lmhead_partials(L.R, dims.V), L.NPs, dims.B, dims.V, tp,
-        rounds, tree_tokens, q, uniforms, L.NC, at<double>(workspace, L.csum),
-        at<double>(workspace, L.psum), at<float>(workspace, L.row_max),
+        rounds, tree_tokens, q, uniforms, L.NC, chunk_sums(workspace, L),
+        at<float>(workspace, L.row_max),
         at<float>(workspace, L.row_sum), at<char>(workspace, L.tstate),
         at<int32_t>(workspace, L.counters), out_tokens, n_accepted, path_nodes,
         at<int32_t>(workspace, L.status), s);

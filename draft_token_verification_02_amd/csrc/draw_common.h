@@ -15,8 +15,21 @@ namespace sv {
 
 namespace {
 
+// exp(x) for x <= 0 as 2^(x log2 e) on the hardware exponential.  Its
+// relative error is about |x| * 2^-23 from rounding x log2 e, plus the
+// instruction's own ulp: below 2e-6 for every x down to -16, and further
+// down the result is itself below 1.2e-7, so its absolute error is
+// negligible next to the terms it is summed with.
+__device__ __forceinline__ float exp_nonpos(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
+// The target's probability of a token, exp(l - M) / S with the row's max M
+// and normaliser S: exp_nonpos times the hardware reciprocal of S (one ulp),
+// so its relative error stays near 2e-6 at worst, far inside the 1e-5 the
+// results are held to.
 __device__ __forceinline__ float target_prob(float logit, float row_max, float row_sum) {
-    return expf(logit - row_max) / row_sum;
+    return exp_nonpos(logit - row_max) * __builtin_amdgcn_rcpf(row_sum);
 }
 
 // The drafter's q at the gamma drafted positions of every sequence.
@@ -36,132 +49,175 @@ struct QArg {
 // pattern orders like the value (the LDS chunk merges entries by unsigned max).
 __device__ __forceinline__ float sparse_value(float v) { return v > 0.f ? v : 0.f; }
 
-// Inclusive prefix sum of one double per thread over the workgroup, in a
-// fixed order (Hillis-Steele within each wave, then the wave totals added in
-// wave order).  Returns this thread's inclusive value; *total gets the sum,
-// with the same association as the last thread's value.
-__device__ double block_inclusive_scan(double v, double* total) {
-    __shared__ double s_wave[kBlock / kWave];
+// ---------------------------------------------------------------------------
+// Wave-wide scans on DPP lane moves, which stay in the VALU (a shuffle goes
+// through the LDS crossbar and waits on it): four row_shr steps scan each
+// 16-lane row (Hillis-Steele), then the last lane of rows 0 and 2 is
+// broadcast into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31).  A lane or row with no source reads the identity.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142,
+              kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t identity) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {      // identity +0
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)b, 0u);
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(b >> 32), 0u);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v, float identity) {
+    return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v), __float_as_uint(identity)));
+}
+
+// Inclusive prefix sum within one wave (every scan of this file uses it).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+    v += dpp_f64<kDppRowShr1, 0xf>(v);
+    v += dpp_f64<kDppRowShr2, 0xf>(v);
+    v += dpp_f64<kDppRowShr4, 0xf>(v);
+    v += dpp_f64<kDppRowShr8, 0xf>(v);
+    v += dpp_f64<kDppRowBcast15, 0xa>(v);
+    v += dpp_f64<kDppRowBcast31, 0xc>(v);
+    return v;
+}
+
+// The wave's maximum and sum, valid in lane 63.
+__device__ __forceinline__ float wave_max_last(float v) {
+    v = fmaxf(v, dpp_f32<kDppRowShr1, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowShr2, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowShr4, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowShr8, 0xf>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowBcast15, 0xa>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowBcast31, 0xc>(v, -INFINITY));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v += dpp_f32<kDppRowShr1, 0xf>(v, 0.f);
+    v += dpp_f32<kDppRowShr2, 0xf>(v, 0.f);
+    v += dpp_f32<kDppRowShr4, 0xf>(v, 0.f);
+    v += dpp_f32<kDppRowShr8, 0xf>(v, 0.f);
+    v += dpp_f32<kDppRowBcast15, 0xa>(v, 0.f);
+    v += dpp_f32<kDppRowBcast31, 0xc>(v, 0.f);
+    return v;
+}
+
+// The previous lane's value (lane 0: +0), for an exclusive scan.
+__device__ __forceinline__ double wave_shift_up(double v) { return dpp_f64<kDppWaveShr1, 0xf>(v); }
+
+// Lane L's double (L uniform), in every lane (two readlanes).
+__device__ __forceinline__ double wave_read(double v, int L) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, L);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), L);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Lane 63's double, in every lane (two readlanes).
+__device__ __forceinline__ double wave_last(double v) { return wave_read(v, kWave - 1); }
+
+// The chunk pass's fp64 totals of the draw weights (tw) and of p (tp) of one
+// chunk: per wave of the workgroup (the wave scan's last lane) and over the
+// workgroup (a wave scan of the wave totals), stored into the chunk's entries
+// of cs.  Wave 0 stores every one, so that a release by thread 0 orders all
+// of them.  One barrier; the LDS it uses is its own.
+__device__ __forceinline__ void store_chunk_totals(double tw, double tp, const ChunkSums& cs,
+                                                   size_t chunk) {
+    __shared__ double s_a[kDrawWaves], s_b[kDrawWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const double o = __shfl_up(v, off);
-        if (lane >= off) v += o;
+    tw = wave_inclusive_scan(tw);
+    tp = wave_inclusive_scan(tp);
+    if (lane == kWave - 1) { s_a[wave] = tw; s_b[wave] = tp; }
+    __syncthreads();
+    if (wave == 0) {
+        double x = 0.0, y = 0.0;
+        if (lane < kDrawWaves) {
+            x = s_a[lane];
+            y = s_b[lane];
+            cs.cwave[chunk * kDrawWaves + lane] = x;
+            cs.pwave[chunk * kDrawWaves + lane] = y;
+        }
+        x = wave_inclusive_scan(x);
+        y = wave_inclusive_scan(y);
+        if (lane == kWave - 1) {
+            cs.csum[chunk] = x;
+            cs.psum[chunk] = y;
+        }
     }
-    if (lane == kWave - 1) s_wave[wave] = v;
-    __syncthreads();
-    double before = 0.0, all = 0.0;
-#pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) {
-        if (w < wave) before += s_wave[w];
-        all += s_wave[w];
-    }
-    __syncthreads();
-    *total = all;
-    return wave == 0 ? v : before + v;
 }
 
-// Exclusive prefix: the previous thread's inclusive value (never incl - own).
-__device__ double block_exclusive_scan(double v, double* total) {
-    __shared__ double s_last[kBlock / kWave];
-    const double incl = block_inclusive_scan(v, total);
-    const int lane = threadIdx.x & (kWave - 1);
-    const double up = __shfl_up(incl, 1);
-    if (lane == kWave - 1) s_last[threadIdx.x / kWave] = incl;
-    __syncthreads();
-    const double r = lane > 0 ? up : (threadIdx.x == 0 ? 0.0 : s_last[threadIdx.x / kWave - 1]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ int block_min_int(int v) {
-    __shared__ int s[kBlock / kWave];
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-    if ((threadIdx.x & (kWave - 1)) == 0) s[threadIdx.x / kWave] = v;
-    __syncthreads();
-    int r = s[0];
-#pragma unroll
-    for (int w = 1; w < kBlock / kWave; ++w) r = min(r, s[w]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ int block_max_int(int v) { return -block_min_int(-v); }
 
 // Softmax normalisers (max, sum exp) of rows row0 .. row0+nrows-1 from the
-// LM-head's per-workgroup partials, into r_m[i], r_s[i].  TPR threads of one
-// wave share a row (TPR = 32, 16 or 8, the most that still fits every row in
-// one pass when it can), each loading its 16-byte groups of maxima and sums
-// kBatch at a time before merging them, so a row costs one memory round trip
-// per kBatch * TPR * 4 partials.  Every thread of the workgroup takes part;
-// the caller synchronises before reading the results.
-template <int TPR>
-__device__ void merge_row_partials_t(const float* __restrict__ part_max,
-                                     const float* __restrict__ part_sum, int NP, int NPs,
-                                     size_t row0, int nrows, float* r_m, float* r_s) {
-    constexpr int kRows = kBlock / TPR;          // rows per pass
-    constexpr int kBatch = 8;                    // float4 loads per thread and array in flight
-    const int sub = threadIdx.x % TPR;
-    const int grp = threadIdx.x / TPR;
-    const int n4 = (NP + 3) / 4;
-    for (int i0 = 0; i0 < nrows; i0 += kRows) {
-        const int i = i0 + grp;
-        float m = -INFINITY, s = 0.f;
-        if (i < nrows) {
-            const size_t r = row0 + i;
-            const float4* pm = reinterpret_cast<const float4*>(part_max + r * NPs);
-            const float4* ps = reinterpret_cast<const float4*>(part_sum + r * NPs);
-            for (int j0 = 0; j0 < n4; j0 += kBatch * TPR) {
-                float4 a[kBatch], c[kBatch];
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int jj = j0 + sub + u * TPR;
-                    a[u] = jj < n4 ? pm[jj] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                    c[u] = jj < n4 ? ps[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-                // this batch's max, then its rescaled sum, merged into (m, s)
-                float bm = -INFINITY, bs = 0.f;
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int j = 4 * (j0 + sub + u * TPR);      // entries past NP are padding
-                    if (j + 0 < NP) bm = fmaxf(bm, a[u].x);
-                    if (j + 1 < NP) bm = fmaxf(bm, a[u].y);
-                    if (j + 2 < NP) bm = fmaxf(bm, a[u].z);
-                    if (j + 3 < NP) bm = fmaxf(bm, a[u].w);
-                }
-                if (bm != -INFINITY) {
-#pragma unroll
-                    for (int u = 0; u < kBatch; ++u) {
-                        const int j = 4 * (j0 + sub + u * TPR);
-                        if (j + 0 < NP && a[u].x != -INFINITY) bs += c[u].x * expf(a[u].x - bm);
-                        if (j + 1 < NP && a[u].y != -INFINITY) bs += c[u].y * expf(a[u].y - bm);
-                        if (j + 2 < NP && a[u].z != -INFINITY) bs += c[u].z * expf(a[u].z - bm);
-                        if (j + 3 < NP && a[u].w != -INFINITY) bs += c[u].w * expf(a[u].w - bm);
-                    }
-                }
-                lse_merge(m, s, bm, bs);
-            }
-        }
-#pragma unroll
-        for (int off = 1; off < TPR; off <<= 1) {
-            const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
-            lse_merge(m, s, m2, s2);
-        }
-        if (sub == 0 && i < nrows) { r_m[i] = m; r_s[i] = s; }
-    }
-}
+// LM-head's per-workgroup partials (m_j, s_j), into r_m[i] = M = max_j m_j and
+// r_s[i] = sum_j s_j exp(m_j - M).  One wave per row, rows dealt to the waves
+// in turn: lane l owns the 16-byte groups l, l + 64, l + 128 and l + 192 of
+// the row (NP <= 1024), so a row needs neither LDS nor a barrier: the lane's
+// maximum, the wave's on DPP moves, read from lane 63; then the lane's sum of
+// s_j exp(m_j - M) in group order and the wave's sum.  One memory round trip
+// and one exponential per partial; lane 63 writes the results.  The caller
+// synchronises before reading them.  Always inlined: an out-of-line call
+// starts by waiting for every memory operation in flight, which would put the
+// caller's draft gathers in front of the partial loads.
+constexpr int kMergeGroups = kLmMaxPartials / (4 * kWave);
+static_assert(kMergeGroups * 4 * kWave == kLmMaxPartials, "whole float4 groups per lane");
 
-__device__ void merge_row_partials(const float* __restrict__ part_max,
-                                   const float* __restrict__ part_sum, int NP, int NPs, size_t row0,
-                                   int nrows, float* r_m, float* r_s) {
-    if (nrows <= kBlock / 32)
-        merge_row_partials_t<32>(part_max, part_sum, NP, NPs, row0, nrows, r_m, r_s);
-    else if (nrows <= kBlock / 16)
-        merge_row_partials_t<16>(part_max, part_sum, NP, NPs, row0, nrows, r_m, r_s);
-    else
-        merge_row_partials_t<8>(part_max, part_sum, NP, NPs, row0, nrows, r_m, r_s);
+__device__ __forceinline__ void merge_row_partials(const float* __restrict__ part_max,
+                                                   const float* __restrict__ part_sum, int NP,
+                                                   int NPs, size_t row0, int nrows, float* r_m,
+                                                   float* r_s) {
+    constexpr int NW = kDrawBlock / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int n4 = (NP + 3) / 4;
+    // Row i goes to wave (i + 1) % NW: wave 0 gets no row while there are
+    // fewer than NW, as it is the one that waits on the draft gathers.
+    for (int i = (wave + NW - 1) % NW; i < nrows; i += NW) {
+        const size_t r = row0 + i;
+        const float4* pm = reinterpret_cast<const float4*>(part_max + r * NPs);
+        const float4* ps = reinterpret_cast<const float4*>(part_sum + r * NPs);
+        float4 a[kMergeGroups], c[kMergeGroups];
+#pragma unroll
+        for (int u = 0; u < kMergeGroups; ++u) {
+            const int jj = min(lane + u * kWave, n4 - 1);    // past the end: loaded, masked
+            a[u] = pm[jj];
+            c[u] = ps[jj];
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeGroups; ++u) {
+            const int e = 4 * (lane + u * kWave);
+            a[u].x = e + 0 < NP ? a[u].x : -INFINITY;
+            a[u].y = e + 1 < NP ? a[u].y : -INFINITY;
+            a[u].z = e + 2 < NP ? a[u].z : -INFINITY;
+            a[u].w = e + 3 < NP ? a[u].w : -INFINITY;
+            m = fmaxf(m, fmaxf(fmaxf(a[u].x, a[u].y), fmaxf(a[u].z, a[u].w)));
+        }
+        const float M =
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_max_last(m)), kWave - 1));
+        // entries at -inf are skipped outright, so that M = -inf (an empty
+        // row) gives 0, not NaN
+        auto term = [&](float x, float sj) {
+            return x != -INFINITY ? sj * exp_nonpos(x - M) : 0.f;
+        };
+        float t = 0.f;
+#pragma unroll
+        for (int u = 0; u < kMergeGroups; ++u) {
+            t += term(a[u].x, c[u].x);
+            t += term(a[u].y, c[u].y);
+            t += term(a[u].z, c[u].z);
+            t += term(a[u].w, c[u].w);
+        }
+        t = wave_sum_last(t);
+        if (lane == kWave - 1) { r_m[i] = M; r_s[i] = t; }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -209,7 +265,7 @@ __device__ __forceinline__ DrawRow draw_row(const float* logits, QArg q, int b, 
 // max on the value's bits (values were made non-negative, where the bit
 // order is the value order).  Every thread of the workgroup takes part.
 __device__ void stage_sparse_chunk(const DrawRow& d, int c0, unsigned* s_qc) {
-    for (int j = threadIdx.x; j < kDrawChunk; j += kBlock) s_qc[j] = 0u;
+    for (int j = threadIdx.x; j < kDrawChunk; j += kDrawBlock) s_qc[j] = 0u;
     __syncthreads();
     auto put = [&](int id, float v) {
         const unsigned rel = (unsigned)(id - c0);
@@ -221,18 +277,18 @@ __device__ void stage_sparse_chunk(const DrawRow& d, int c0, unsigned* s_qc) {
         const float4* v4 = reinterpret_cast<const float4*>(d.qvals);
         const int K4 = d.K >> 2;
 #pragma unroll 4
-        for (int j = threadIdx.x; j < K4; j += kBlock) {
+        for (int j = threadIdx.x; j < K4; j += kDrawBlock) {
             const int4 i = id4[j];
             const float4 v = v4[j];
             put(i.x, v.x); put(i.y, v.y); put(i.z, v.z); put(i.w, v.w);
         }
     } else {
-        for (int j = threadIdx.x; j < d.K; j += kBlock) put(d.qids[j], d.qvals[j]);
+        for (int j = threadIdx.x; j < d.K; j += kDrawBlock) put(d.qids[j], d.qvals[j]);
     }
     __syncthreads();
 }
 
-__device__ __forceinline__ void load16(const float* row, int j0, int V, float (&x)[kDrawPerThread]) {
+__device__ __forceinline__ void load_run(const float* row, int j0, int V, float (&x)[kDrawPerThread]) {
     if (((V & 3) == 0) && j0 + kDrawPerThread <= V) {
 #pragma unroll
         for (int e = 0; e < kDrawPerThread; e += 4) {
@@ -248,14 +304,14 @@ __device__ __forceinline__ void load16(const float* row, int j0, int V, float (&
     }
 }
 
-// Draw weights w and target probabilities p of 16 consecutive tokens from j0
+// Draw weights w and target probabilities p of the kDrawPerThread tokens from j0
 // (zero past the end of the vocabulary).  With sparse q, s_qc holds the
 // chunk starting at c0 (stage_sparse_chunk).
 template <bool SPARSE>
-__device__ __forceinline__ void draw_weights16(const DrawRow& d, int j0, const unsigned* s_qc, int c0,
+__device__ __forceinline__ void draw_weights(const DrawRow& d, int j0, const unsigned* s_qc, int c0,
                                                float (&w)[kDrawPerThread], float (&p)[kDrawPerThread]) {
     float l[kDrawPerThread], qv[kDrawPerThread];
-    load16(d.lrow, j0, d.V, l);
+    load_run(d.lrow, j0, d.V, l);
     const bool has_q = d.has_q();
     if (SPARSE) {
         if (has_q) {
@@ -268,7 +324,7 @@ __device__ __forceinline__ void draw_weights16(const DrawRow& d, int j0, const u
             }
         }
     } else if (has_q) {
-        load16(d.qrow, j0, d.V, qv);
+        load_run(d.qrow, j0, d.V, qv);
     }
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) {
@@ -278,67 +334,211 @@ __device__ __forceinline__ void draw_weights16(const DrawRow& d, int j0, const u
     }
 }
 
-// The inverse-CDF draw for sequence b from its chunk totals.  Returns the
-// token; *flags gets SV_DEV_FALLBACK / SV_DEV_NONFINITE.
-template <bool SPARSE>
-__device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* psum, float u,
-                    unsigned* s_qc, int* flags) {
-    __shared__ double s_before;
-    // Thread t owns chunks [t*per, (t+1)*per) of the chunk totals.
-    const int per = (NC + kBlock - 1) / kBlock;
-    const int c0 = threadIdx.x * per, c1 = min(NC, c0 + per);
-
-    // Total draw weight S; fall back to p when the residual carries none.
-    const double* sums = csum + (size_t)b * NC;
-    double own = 0.0, S;
-    for (int c = c0; c < c1; ++c) own += sums[c];
-    double excl = block_exclusive_scan(own, &S);
-    *flags = 0;
-    if (!(S > 0.0)) {
-        *flags = SV_DEV_FALLBACK;
-        d.drop_q();
-        sums = psum + (size_t)b * NC;
-        own = 0.0;
-        for (int c = c0; c < c1; ++c) own += sums[c];
-        excl = block_exclusive_scan(own, &S);
-    }
-    if (!(S > 0.0) || !(S < INFINITY)) {
-        *flags |= SV_DEV_NONFINITE;
-        return 0;
-    }
-    const double t = (double)u * S;
-
-    // The first chunk whose running sum reaches t and that carries weight;
-    // failing that (only through rounding), the last chunk with weight.
-    int first = INT_MAX, last_pos = -1;
-    double run = excl;
-    for (int c = c0; c < c1; ++c) {
-        run += sums[c];
-        if (sums[c] > 0.0) {
-            last_pos = c;
-            if (first == INT_MAX && run >= t) first = c;
-        }
-    }
-    int chunk = block_min_int(first);
-    if (chunk == INT_MAX) chunk = block_max_int(last_pos);
-    if (c0 <= chunk && chunk < c1) {          // its owner: running sum before it, same order
-        double r = excl;
-        for (int c = c0; c < chunk; ++c) r += sums[c];
-        s_before = r;
+// The last-workgroup pattern of the fused draw and tree rounds: thread 0
+// publishes its chunk totals with a release increment of the sequence's
+// counter, and the workgroup that brings it to NC takes an acquire fence
+// (agent scope) before anyone reads the other chunks' totals.  Only thread
+// 0 fences; the workgroup barrier after it orders every thread's later
+// reads.  Returns, in every thread, whether this is the last workgroup.
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int NC) {
+    __shared__ int s_last;
+    if (threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = done == NC - 1;
+        if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    const double before = s_before;
+    return s_last;
+}
 
-    // Rescan that chunk in token order.
-    const int cs = chunk * kDrawChunk;
-    if (SPARSE && d.has_q()) stage_sparse_chunk(d, cs, s_qc);
-    const int j0 = cs + threadIdx.x * kDrawPerThread;
+// ---------------------------------------------------------------------------
+// The pick, on one wave (wave 0 of the sequence's last workgroup): the sum S
+// of the chunk totals, the chunk where the running sum reaches t = u S, then
+// the wave of that chunk's workgroup from the wave totals the chunk pass
+// left, then a rescan of that wave's 64 * kDrawPerThread tokens.  Each level
+// takes the first entry with weight whose running sum reaches t, failing
+// that (only through rounding) the last entry with weight.
+
+// S, the sum of one sequence's chunk totals tot[0, NC): lanes own chunks, 64
+// at a time, each window a wave scan, the windows added in order.  Every
+// lane of the calling wave gets S.
+__device__ __forceinline__ double chunk_total_sum(const double* tot, int NC) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double S = 0.0;
+    for (int w0 = 0; w0 < NC; w0 += kWave) {
+        double own = 0.0;
+        if (w0 + lane < NC) own += tot[w0 + lane];
+        S += wave_last(wave_inclusive_scan(own));
+    }
+    return S;
+}
+
+// Where the running sum over n entries val (lane-owned, zero past the end)
+// first reaches t from the offset carry: the lane and the running sum before
+// it, or lane -1 when no entry with weight reaches it (*last_lane, *last_base
+// then name the last entry with weight, if any).
+struct Crossing {
+    int lane;
+    double base;
+};
+
+__device__ __forceinline__ Crossing crossing(double val, double carry, double t, int* last_lane,
+                                             double* last_base, double* total) {
+    const double incl = wave_inclusive_scan(val);
+    const double base = carry + wave_shift_up(incl);
+    *total = wave_last(incl);
+    const unsigned long long reach = __ballot(val > 0.0 && base + val >= t);
+    const unsigned long long any = __ballot(val > 0.0);
+    if (any) {
+        *last_lane = 63 - __builtin_clzll(any);
+        *last_base = wave_read(base, *last_lane);
+    }
+    if (!reach) return {-1, 0.0};
+    const int l = __builtin_ctzll(reach);
+    return {l, wave_read(base, l)};
+}
+
+// The dense q of tokens [c0, c0 + kWave * kDrawPerThread) of a sparse row,
+// built in s_qc by one wave: zeroed, then every entry whose id falls in the
+// range merged in by unsigned max on the value's bits (values were made
+// non-negative, where the bit order is the value order).  One wave's LDS
+// operations take effect in order, so the zeros land before the merges.
+__device__ void stage_sparse_wave(const DrawRow& d, int c0, unsigned* s_qc) {
+    constexpr int n = kWave * kDrawPerThread;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int j = lane; j < n; j += kWave) s_qc[j] = 0u;
+    auto put = [&](int id, float v) {
+        const unsigned rel = (unsigned)(id - c0);
+        if (id >= 0 && id < d.V && rel < (unsigned)n)
+            atomicMax(&s_qc[rel], __float_as_uint(sparse_value(v)));
+    };
+    if ((d.K & 3) == 0) {
+        const int4* id4 = reinterpret_cast<const int4*>(d.qids);
+        const float4* v4 = reinterpret_cast<const float4*>(d.qvals);
+        const int K4 = d.K >> 2;
+#pragma unroll 4
+        for (int j = lane; j < K4; j += kWave) {
+            const int4 i = id4[j];
+            const float4 v = v4[j];
+            put(i.x, v.x); put(i.y, v.y); put(i.z, v.z); put(i.w, v.w);
+        }
+    } else {
+        for (int j = lane; j < d.K; j += kWave) put(d.qids[j], d.qvals[j]);
+    }
+}
+
+// The inverse-CDF draw for sequence b from the chunk and wave totals.  Called
+// by one whole wave; every lane returns the token.  *flags gets
+// SV_DEV_FALLBACK (the residual carried no weight: drawn from p) and
+// SV_DEV_NONFINITE (no finite positive total at all: token 0).  s_qc holds,
+// for sparse q, kWave * kDrawPerThread words of LDS.
+template <bool SPARSE>
+__device__ int pick(DrawRow d, int b, int NC, const ChunkSums& cs, float u, unsigned* s_qc,
+                    int* flags) {
+    __shared__ double s_wv[kDrawWaves];
+    const int lane = threadIdx.x & (kWave - 1);
+    *flags = 0;
+    const double* tot = cs.csum + (size_t)b * NC;
+    const double* wtot = cs.cwave + (size_t)b * NC * kDrawWaves;
+    auto fall_back = [&]() {                   // no residual mass: draw from p
+        *flags = SV_DEV_FALLBACK;
+        d.drop_q();
+        tot = cs.psum + (size_t)b * NC;
+        wtot = cs.pwave + (size_t)b * NC * kDrawWaves;
+    };
+    double t, before, wt = 0.0;
+    int chunk;
+    if (NC <= kWave) {
+        // One window (V <= 262144): lane c loads chunk c's total and its wave
+        // totals in the same round trip.
+        double own, wv[kDrawWaves];
+        auto load = [&]() {
+            own = 0.0;
+#pragma unroll
+            for (int k = 0; k < kDrawWaves; ++k) wv[k] = 0.0;
+            if (lane < NC) {
+                own += tot[lane];
+                const double2* src = reinterpret_cast<const double2*>(wtot + (size_t)lane * kDrawWaves);
+#pragma unroll
+                for (int k = 0; k < kDrawWaves; k += 2) {
+                    const double2 v = src[k / 2];
+                    wv[k] = v.x;
+                    wv[k + 1] = v.y;
+                }
+            }
+        };
+        load();
+        double incl = wave_inclusive_scan(own);
+        double S = 0.0 + wave_last(incl);      // the association of chunk_total_sum
+        if (!(S > 0.0)) {
+            fall_back();
+            load();
+            incl = wave_inclusive_scan(own);
+            S = 0.0 + wave_last(incl);
+        }
+        if (!(S > 0.0) || !(S < INFINITY)) {
+            *flags |= SV_DEV_NONFINITE;
+            return 0;
+        }
+        t = (double)u * S;
+        const double base = 0.0 + wave_shift_up(incl);
+        const unsigned long long reach = __ballot(own > 0.0 && base + own >= t);
+        const unsigned long long any = __ballot(own > 0.0);
+        chunk = reach ? __builtin_ctzll(reach) : any ? 63 - __builtin_clzll(any) : 0;
+        before = wave_read(base, chunk);
+        // lane k takes wave total k of the chunk, handed over through LDS
+        // (one wave's LDS writes land before its later reads)
+        if (lane == chunk) {
+#pragma unroll
+            for (int k = 0; k < kDrawWaves; ++k) s_wv[k] = wv[k];
+        }
+        if (lane < kDrawWaves) wt = s_wv[lane];
+    } else {
+        double S = chunk_total_sum(tot, NC);
+        if (!(S > 0.0)) {
+            fall_back();
+            S = chunk_total_sum(tot, NC);
+        }
+        if (!(S > 0.0) || !(S < INFINITY)) {
+            *flags |= SV_DEV_NONFINITE;
+            return 0;
+        }
+        t = (double)u * S;
+        int last = 0;
+        double last_base = 0.0, carry = 0.0;
+        chunk = -1;
+        before = 0.0;
+        for (int w0 = 0; w0 < NC && chunk < 0; w0 += kWave) {
+            double own = 0.0, total;
+            if (w0 + lane < NC) own += tot[w0 + lane];
+            int ll = -1;
+            double lb = 0.0;
+            const Crossing x = crossing(own, carry, t, &ll, &lb, &total);
+            if (ll >= 0) { last = w0 + ll; last_base = lb; }
+            if (x.lane >= 0) { chunk = w0 + x.lane; before = x.base; }
+            carry += total;
+        }
+        if (chunk < 0) { chunk = last; before = last_base; }
+        if (lane < kDrawWaves) wt = wtot[(size_t)chunk * kDrawWaves + lane];
+    }
+
+    // The wave of the chunk's workgroup.
+    int wl = 0;
+    double wb = before, total;
+    const Crossing x = crossing(wt, before, t, &wl, &wb, &total);
+    const int sub = x.lane >= 0 ? x.lane : wl;
+    const double base_w = x.lane >= 0 ? x.base : wb;
+
+    // Its tokens, rescanned in order.
+    const int c0 = chunk * kDrawChunk + sub * kWave * kDrawPerThread;
+    if (SPARSE && d.has_q()) stage_sparse_wave(d, c0, s_qc);
+    const int j0 = c0 + lane * kDrawPerThread;
     float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights16<SPARSE>(d, j0, s_qc, cs, w, p);
-    double mine = 0.0, chunk_total;
+    draw_weights<SPARSE>(d, j0, s_qc, c0, w, p);
+    double mine = 0.0;
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) mine += (double)w[e];
-    const double base = before + block_exclusive_scan(mine, &chunk_total);
+    const double base = base_w + wave_shift_up(wave_inclusive_scan(mine));
     int y = INT_MAX, ylast = -1;
     double part = 0.0;
 #pragma unroll
@@ -349,9 +549,11 @@ __device__ int pick(DrawRow d, int b, int NC, const double* csum, const double* 
             if (y == INT_MAX && base + part >= t) y = j0 + e;
         }
     }
-    int tok = block_min_int(y);
-    if (tok == INT_MAX) tok = block_max_int(ylast);
-    return tok;
+    // Lanes cover ascending tokens: the first candidate sits in the lowest
+    // lane that has one, the last token with weight in the highest.
+    const unsigned long long hit = __ballot(y != INT_MAX), pos = __ballot(ylast >= 0);
+    if (hit) return __builtin_amdgcn_readlane(y, __builtin_ctzll(hit));
+    return pos ? __builtin_amdgcn_readlane(ylast, 63 - __builtin_clzll(pos)) : c0;
 }
 
 }  // namespace

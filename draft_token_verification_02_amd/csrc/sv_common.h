@@ -15,7 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes = 8 bf16
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;              // threads per workgroup of the draw kernel
+constexpr int kBlock = 256;              // threads per greedy and drafter-head workgroup
 
 constexpr int kLmTile = 16;              // vocab rows (and hidden rows) per MFMA fragment
 #ifndef SV_LM_WAVES
@@ -24,8 +24,17 @@ constexpr int kLmTile = 16;              // vocab rows (and hidden rows) per MFM
 constexpr int kLmWaves = SV_LM_WAVES;    // waves per LM-head workgroup
 constexpr int kLmMaxPartials = 1024;     // LM-head workgroups (softmax partials per row), at most
 constexpr int kLmRowsPerPass = 64;       // hidden rows one LM-head launch handles
-constexpr int kDrawPerThread = 16;       // vocab entries per thread in the draw kernel
-constexpr int kDrawChunk = kBlock * kDrawPerThread;                             // 4096
+// Draw and tree kernels: 1024 threads (four waves per SIMD, so that one
+// wave's dependent arithmetic hides behind the others') over 4096-token
+// chunks, four tokens per thread.
+#ifndef SV_DRAW_BLOCK
+#define SV_DRAW_BLOCK 1024
+#endif
+constexpr int kDrawBlock = SV_DRAW_BLOCK;
+constexpr int kDrawChunk = 4096;                                                // tokens per chunk
+constexpr int kDrawPerThread = kDrawChunk / kDrawBlock;
+constexpr int kDrawWaves = kDrawBlock / kWave;
+static_assert(kDrawPerThread % 4 == 0, "whole 16-byte runs of tokens per thread");
 
 // LM-head workgroups worth launching for a vocabulary of V: at least one
 // 16-row fragment per wave.
@@ -49,7 +58,17 @@ static inline bool lmhead_use_tiled(int R, int V) {
 struct Layout {
     int R, NPs, NC;
     size_t logits, part_max, part_sum, part_arg, row_max, row_sum, status, counters, csum, psum,
-        tstate, total;
+        cwave, pwave, tstate, total;
+};
+
+// The draw's chunk totals, fp64: per (sequence, chunk) the sums of the draw
+// weights (csum [B][NC]) and of p (psum), and the same per wave of the
+// chunk's workgroup (cwave, pwave [B][NC][kDrawWaves]).
+struct ChunkSums {
+    double* csum;
+    double* psum;
+    double* cwave;
+    double* pwave;
 };
 
 constexpr size_t kTreeStateBytes = 32;   // per-sequence walk state of tree verification
@@ -76,6 +95,8 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     L.counters = off; off = align_up(off + (size_t)B * sizeof(int32_t), 256);
     L.csum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
     L.psum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
+    L.cwave = off;    off = align_up(off + (size_t)B * L.NC * kDrawWaves * sizeof(double), 256);
+    L.pwave = off;    off = align_up(off + (size_t)B * L.NC * kDrawWaves * sizeof(double), 256);
     L.tstate = off;   off = align_up(off + (size_t)B * kTreeStateBytes, 256);
     L.total = off;
     return L;

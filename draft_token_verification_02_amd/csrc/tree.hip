@@ -134,7 +134,7 @@ __device__ __forceinline__ DrawRow tree_draw_row(const TreeState& st, const Tree
     return d;
 }
 
-__global__ __launch_bounds__(kBlock) void tree_init_kernel(
+__global__ __launch_bounds__(kDrawBlock) void tree_init_kernel(
     const float* __restrict__ part_max, const float* __restrict__ part_sum, int NP, int NPs,
     TreeTopo tp, TreeArgs a, float* __restrict__ row_max, float* __restrict__ row_sum,
     TreeState* __restrict__ state, int32_t* __restrict__ n_accepted,
@@ -143,12 +143,12 @@ __global__ __launch_bounds__(kBlock) void tree_init_kernel(
     const int b = blockIdx.x;
     const int T1 = tp.T + 1;
     merge_row_partials(part_max, part_sum, NP, NPs, (size_t)b * T1, T1, r_m, r_s);
-    for (int i = threadIdx.x; i <= tp.D; i += kBlock) {
+    for (int i = threadIdx.x; i <= tp.D; i += kDrawBlock) {
         a.out_tokens[(size_t)b * (tp.D + 1) + i] = -1;
         if (a.path_nodes && i < tp.D) a.path_nodes[(size_t)b * tp.D + i] = -1;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < T1; i += kBlock) {
+    for (int i = threadIdx.x; i < T1; i += kDrawBlock) {
         row_max[(size_t)b * T1 + i] = r_m[i];
         row_sum[(size_t)b * T1 + i] = r_s[i];
     }
@@ -169,60 +169,47 @@ __global__ __launch_bounds__(kBlock) void tree_init_kernel(
 
 // Chunk c's totals of the weights at the sequence's current row:
 // max(0, p - c q) (the residual of a pending test, or the draw's), or p for a
-// bonus draw.  Every thread takes part; thread 0 stores them.
+// bonus draw, per wave and over the workgroup.  Every thread takes part.
 __device__ void tree_chunk_totals(const TreeState& st, const TreeTopo& tp, int b, int c, int NC,
-                                  const TreeArgs& a, double* __restrict__ csum,
-                                  double* __restrict__ psum) {
+                                  const TreeArgs& a, const ChunkSums& cs) {
     const DrawRow d = tree_draw_row(st, tp, b, a);
-    const int cs = c * kDrawChunk;
+    const int c0 = c * kDrawChunk;
     float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights16<false>(d, cs + threadIdx.x * kDrawPerThread, nullptr, cs, w, p);
+    draw_weights<false>(d, c0 + threadIdx.x * kDrawPerThread, nullptr, c0, w, p);
     double tw = 0.0, tp_ = 0.0;
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp_ += (double)p[e]; }
-    double tot_w, tot_p;
-    block_inclusive_scan(tw, &tot_w);
-    block_inclusive_scan(tp_, &tot_p);
-    if (threadIdx.x == 0) {
-        csum[(size_t)b * NC + c] = tot_w;
-        psum[(size_t)b * NC + c] = tot_p;
-    }
+    store_chunk_totals(tw, tp_, cs, (size_t)b * NC + c);
 }
 
 // With every chunk total of the round in place: the sum S, then either the
 // pending sibling test and the walk onwards (state updated for the next
-// round), or the inverse-CDF pick that ends the sequence.  Every thread takes
-// part (the pick is a workgroup operation).
+// round), or the inverse-CDF pick that ends the sequence.  One whole wave
+// (the pick is a wave operation; lane 0 updates the state).
 __device__ void tree_decide(TreeState st, const TreeTopo& tp, int b, const TreeArgs& a, int NC,
-                            const double* __restrict__ csum, const double* __restrict__ psum,
-                            TreeState* __restrict__ state, int32_t* __restrict__ n_accepted,
-                            int32_t* __restrict__ status) {
-    __shared__ int s_draw;
+                            const ChunkSums& cs, TreeState* __restrict__ state,
+                            int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
+    const int lane = threadIdx.x & (kWave - 1);
     const DrawRow d = tree_draw_row(st, tp, b, a);
-    // S in the association the pick uses (thread-owned runs of chunks, then a scan)
-    const int per = (NC + kBlock - 1) / kBlock;
-    const int c0 = threadIdx.x * per, c1 = min(NC, c0 + per);
-    double own = 0.0, S;
-    for (int c = c0; c < c1; ++c) own += csum[(size_t)b * NC + c];
-    block_exclusive_scan(own, &S);
-    if (threadIdx.x == 0) {
-        int draw = st.phase != kPhaseSum;
-        if (!draw && !(S > 0.0 && S < INFINITY)) draw = 1;   // no residual mass: the pick falls back to p
-        if (!draw) {
+    // S in the association the pick uses; every lane has it, so every lane
+    // takes the same branch.
+    const double S = chunk_total_sum(cs.csum + (size_t)b * NC, NC);
+    bool draw = st.phase != kPhaseSum;
+    if (!draw && !(S > 0.0 && S < INFINITY)) draw = true;   // no residual mass: the pick falls back to p
+    if (!draw) {
+        if (lane == 0) {
             const size_t g0 = grow(b, tp, 0);
             tree_advance(st, S, tp, b, a, a.row_max + g0, a.row_sum + g0);
             state[b] = st;
             n_accepted[b] = st.depth;
             status[b] = st.flags;
         }
-        s_draw = draw;
+        return;
     }
-    __syncthreads();
-    if (!s_draw) return;
     int pflags;
-    const int tok = pick<false>(d, b, NC, csum, psum, a.uniforms[(size_t)b * (tp.T + 1) + tp.T],
-                                nullptr, &pflags);
-    if (threadIdx.x == 0) {
+    const int tok = pick<false>(d, b, NC, cs, a.uniforms[(size_t)b * (tp.T + 1) + tp.T], nullptr,
+                                &pflags);
+    if (lane == 0) {
         a.out_tokens[(size_t)b * (tp.D + 1) + st.depth] = tok;
         n_accepted[b] = st.depth;
         status[b] = st.flags | pflags;
@@ -233,46 +220,39 @@ __device__ void tree_decide(TreeState st, const TreeTopo& tp, int b, const TreeA
 
 // Split round, many sequences: chunk totals here, tree_decide_kernel next
 // (the kernel boundary orders the totals before the decision).
-__global__ __launch_bounds__(kBlock) void tree_sums_kernel(
-    TreeTopo tp, TreeArgs a, const TreeState* __restrict__ state, int NC,
-    double* __restrict__ csum, double* __restrict__ psum) {
+__global__ __launch_bounds__(kDrawBlock) void tree_sums_kernel(
+    TreeTopo tp, TreeArgs a, const TreeState* __restrict__ state, int NC, ChunkSums cs) {
     const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
     const TreeState st = state[b];
     if (st.phase == kPhaseDone) return;
-    tree_chunk_totals(st, tp, b, c, NC, a, csum, psum);
+    tree_chunk_totals(st, tp, b, c, NC, a, cs);
 }
 
-__global__ __launch_bounds__(kBlock) void tree_decide_kernel(
-    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, const double* __restrict__ csum,
-    const double* __restrict__ psum, int32_t* __restrict__ n_accepted,
-    int32_t* __restrict__ status) {
+// One wave per sequence.
+__global__ __launch_bounds__(kWave) void tree_decide_kernel(
+    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, ChunkSums cs,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
     const int b = blockIdx.x;
     const TreeState st = state[b];
     if (st.phase == kPhaseDone) return;
-    tree_decide(st, tp, b, a, NC, csum, psum, state, n_accepted, status);
+    tree_decide(st, tp, b, a, NC, cs, state, n_accepted, status);
 }
 
 // Fused round, few sequences: the sequence's last chunk workgroup to finish
 // (a per-sequence counter that the LM-head launch zeroes and this kernel
 // resets) decides -- one launch per round.
-__global__ __launch_bounds__(kBlock) void tree_round_kernel(
-    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, double* __restrict__ csum,
-    double* __restrict__ psum, int32_t* __restrict__ counters, int32_t* __restrict__ n_accepted,
+__global__ __launch_bounds__(kDrawBlock) void tree_round_kernel(
+    TreeTopo tp, TreeArgs a, TreeState* __restrict__ state, int NC, ChunkSums cs,
+    int32_t* __restrict__ counters, int32_t* __restrict__ n_accepted,
     int32_t* __restrict__ status) {
-    __shared__ int s_last;
     const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
     const TreeState st = state[b];
     if (st.phase == kPhaseDone) return;
-    tree_chunk_totals(st, tp, b, c, NC, a, csum, psum);
-    if (threadIdx.x == 0) {
-        __threadfence();                       // publish the totals before counting
-        s_last = atomicAdd(&counters[b], 1) == NC - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();                           // see every other chunk's totals
+    tree_chunk_totals(st, tp, b, c, NC, a, cs);
+    if (!arrive_last(&counters[b], NC)) return;
+    if (threadIdx.x >= kWave) return;          // the decision is one wave's
     if (threadIdx.x == 0) counters[b] = 0;     // ready for the next round
-    tree_decide(st, tp, b, a, NC, csum, psum, state, n_accepted, status);
+    tree_decide(st, tp, b, a, NC, cs, state, n_accepted, status);
 }
 
 }  // namespace
@@ -284,12 +264,12 @@ __global__ __launch_bounds__(kBlock) void tree_round_kernel(
 hipError_t launch_tree(const float* logits, const float* part_max, const float* part_sum, int NP,
                        int NPs, int B, int V, const TreeTopo& tp, int rounds,
                        const int32_t* tokens, const float* q, const float* uniforms, int NC,
-                       double* csum, double* psum, float* row_max, float* row_sum, void* state,
+                       const ChunkSums& cs, float* row_max, float* row_sum, void* state,
                        int32_t* counters, int32_t* out_tokens, int32_t* n_accepted,
                        int32_t* path_nodes, int32_t* status, hipStream_t stream) {
     TreeArgs a{logits, row_max, row_sum, tokens, q, uniforms, V, out_tokens, path_nodes};
     TreeState* st = static_cast<TreeState*>(state);
-    tree_init_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(part_max, part_sum, NP, NPs, tp, a,
+    tree_init_kernel<<<dim3(B), dim3(kDrawBlock), 0, stream>>>(part_max, part_sum, NP, NPs, tp, a,
                                                           row_max, row_sum, st, n_accepted,
                                                           status);
     hipError_t e = hipGetLastError();
@@ -299,16 +279,16 @@ hipError_t launch_tree(const float* logits, const float* part_max, const float* 
     const bool fused = groups <= SV_TREE_FUSE_MAX_GROUPS;
     for (int r = 0; r < rounds && e == hipSuccess; ++r) {
         if (fused) {
-            tree_round_kernel<<<dim3(groups), dim3(kBlock), 0, stream>>>(
-                tp, a, st, NC, csum, psum, counters, n_accepted, status);
+            tree_round_kernel<<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+                tp, a, st, NC, cs, counters, n_accepted, status);
             e = hipGetLastError();
             continue;
         }
-        tree_sums_kernel<<<dim3(groups), dim3(kBlock), 0, stream>>>(tp, a, st, NC, csum, psum);
+        tree_sums_kernel<<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(tp, a, st, NC, cs);
         e = hipGetLastError();
         if (e != hipSuccess) break;
-        tree_decide_kernel<<<dim3(B), dim3(kBlock), 0, stream>>>(tp, a, st, NC, csum, psum,
-                                                                n_accepted, status);
+        tree_decide_kernel<<<dim3(B), dim3(kWave), 0, stream>>>(tp, a, st, NC, cs, n_accepted,
+                                                                status);
         e = hipGetLastError();
     }
     return e;

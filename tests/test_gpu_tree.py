@@ -48,6 +48,7 @@ SMALL = [  # (B, parent, d, V, sigma, seed)
     (40, [-1, -1, 0, 1, 1], 32, 5000, 1.5, 5),      # many sequences
     (2, [-1] * 12, 48, 300, 2.0, 6),                # one wide fork
     (4, list(range(-1, 19)) + [0, 1], 64, 777, 0.5, 7),   # deep, two side branches
+    (1, [-1, -1, 0, 0], 32, 280000, 1.0, 8),       # 69 chunks: split rounds, multi-window S
 ]
 
 
