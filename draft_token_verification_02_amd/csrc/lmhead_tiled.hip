@@ -156,6 +156,10 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
 #pragma unroll
             for (int b = 0; b < kFR; ++b)
                 fb[b] = *reinterpret_cast<const u32x4*>(lh + b * kLmTile * kRowBytes + ks * 64);
+            // Every fragment read is issued before the first MFMA: left to
+            // itself the compiler reuses one register quad for the A
+            // fragments and waits out each read in turn (about 8% slower).
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < kFV; ++a)
 #pragma unroll
