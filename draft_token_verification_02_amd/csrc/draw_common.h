@@ -401,29 +401,42 @@ __device__ __forceinline__ Crossing crossing(double val, double carry, double t,
 // The dense q of tokens [c0, c0 + kWave * kDrawPerThread) of a sparse row,
 // built in s_qc by one wave: zeroed, then every entry whose id falls in the
 // range merged in by unsigned max on the value's bits (values were made
-// non-negative, where the bit order is the value order).  One wave's LDS
-// operations take effect in order, so the zeros land before the merges.
+// non-negative, where the bit order is the value order).  The ids go first,
+// kSparseBatch 16-byte groups per lane at a time; a value is loaded only for
+// an id in the range (a few per row).  One wave's LDS operations take effect
+// in order, so the zeros land before the merges.
+constexpr int kSparseBatch = 8;
+
 __device__ void stage_sparse_wave(const DrawRow& d, int c0, unsigned* s_qc) {
     constexpr int n = kWave * kDrawPerThread;
     const int lane = threadIdx.x & (kWave - 1);
     for (int j = lane; j < n; j += kWave) s_qc[j] = 0u;
-    auto put = [&](int id, float v) {
-        const unsigned rel = (unsigned)(id - c0);
-        if (id >= 0 && id < d.V && rel < (unsigned)n)
-            atomicMax(&s_qc[rel], __float_as_uint(sparse_value(v)));
+    auto in_range = [&](int id) {
+        return id >= 0 && id < d.V && (unsigned)(id - c0) < (unsigned)n;
     };
+    auto put = [&](int id, float v) { atomicMax(&s_qc[id - c0], __float_as_uint(sparse_value(v))); };
     if ((d.K & 3) == 0) {
         const int4* id4 = reinterpret_cast<const int4*>(d.qids);
-        const float4* v4 = reinterpret_cast<const float4*>(d.qvals);
         const int K4 = d.K >> 2;
-#pragma unroll 4
-        for (int j = lane; j < K4; j += kWave) {
-            const int4 i = id4[j];
-            const float4 v = v4[j];
-            put(i.x, v.x); put(i.y, v.y); put(i.z, v.z); put(i.w, v.w);
+        for (int j0 = 0; j0 < K4; j0 += kSparseBatch * kWave) {
+            int4 ids[kSparseBatch];
+#pragma unroll
+            for (int u = 0; u < kSparseBatch; ++u) {
+                const int j = j0 + lane + u * kWave;
+                ids[u] = j < K4 ? id4[j] : make_int4(-1, -1, -1, -1);
+            }
+#pragma unroll
+            for (int u = 0; u < kSparseBatch; ++u) {
+                const int e = 4 * (j0 + lane + u * kWave);
+                if (in_range(ids[u].x)) put(ids[u].x, d.qvals[e + 0]);
+                if (in_range(ids[u].y)) put(ids[u].y, d.qvals[e + 1]);
+                if (in_range(ids[u].z)) put(ids[u].z, d.qvals[e + 2]);
+                if (in_range(ids[u].w)) put(ids[u].w, d.qvals[e + 3]);
+            }
         }
     } else {
-        for (int j = lane; j < d.K; j += kWave) put(d.qids[j], d.qvals[j]);
+        for (int j = lane; j < d.K; j += kWave)
+            if (in_range(d.qids[j])) put(d.qids[j], d.qvals[j]);
     }
 }
 
