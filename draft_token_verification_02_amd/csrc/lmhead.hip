@@ -77,21 +77,11 @@ namespace {
 #ifndef SV_LM4_U
 #define SV_LM4_U 2
 #endif
-#ifndef SV_LM8_T
-#define SV_LM8_T 4
-#endif
-#ifndef SV_LM8_U
-#define SV_LM8_U 2
-#endif
 template <int MT> struct LmCfg;
 template <> struct LmCfg<1> { static constexpr int T = SV_LM1_T, U = SV_LM1_U; };
 template <> struct LmCfg<2> { static constexpr int T = SV_LM2_T, U = SV_LM2_U; };
 template <> struct LmCfg<3> { static constexpr int T = SV_LM3_T, U = SV_LM3_U; };
 template <> struct LmCfg<4> { static constexpr int T = SV_LM4_T, U = SV_LM4_U; };
-template <> struct LmCfg<5> { static constexpr int T = SV_LM8_T, U = SV_LM8_U; };
-template <> struct LmCfg<6> { static constexpr int T = SV_LM8_T, U = SV_LM8_U; };
-template <> struct LmCfg<7> { static constexpr int T = SV_LM8_T, U = SV_LM8_U; };
-template <> struct LmCfg<8> { static constexpr int T = SV_LM8_T, U = SV_LM8_U; };
 constexpr int kGenericU = 4;         // ring depth of the path for ragged d
 
 // Groups of T fragments a wave stages in LDS before writing them out: a
@@ -447,15 +437,7 @@ hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d
             case 1: launch_mt<1>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
             case 2: launch_mt<2>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
             case 3: launch_mt<3>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            case 4: launch_mt<4>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-#if SV_LM_ROWS_PER_PASS > 64
-            case 5: launch_mt<5>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            case 6: launch_mt<6>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            case 7: launch_mt<7>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            default: launch_mt<8>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-#else
             default: launch_mt<4>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-#endif
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -23,10 +23,7 @@ constexpr int kLmTile = 16;              // vocab rows (and hidden rows) per MFM
 #endif
 constexpr int kLmWaves = SV_LM_WAVES;    // waves per LM-head workgroup
 constexpr int kLmMaxPartials = 1024;     // LM-head workgroups (softmax partials per row), at most
-#ifndef SV_LM_ROWS_PER_PASS
-#define SV_LM_ROWS_PER_PASS 64
-#endif
-constexpr int kLmRowsPerPass = SV_LM_ROWS_PER_PASS;   // hidden rows one LM-head launch handles
+constexpr int kLmRowsPerPass = 64;       // hidden rows one LM-head launch handles
 // Draw and tree kernels: 1024 threads (four waves per SIMD, so that one
 // wave's dependent arithmetic hides behind the others') over 4096-token
 // chunks, four tokens per thread.
