@@ -54,62 +54,63 @@ constexpr int kRowBytes = kTK * 2 + 16;            // padded LDS row: 144 bytes
 constexpr int kXcds = 8;
 
 // ---------------------------------------------------------------------------
-// R > 128: 256 x 256 blocks, 8 waves of 128 x 64, both operands staged in LDS.
-constexpr int kBigTR = 256;          // hidden rows per workgroup
+// R > 128: 256 x TR blocks (TR = 128, 192 or 256 rows, whichever pads R
+// least), 8 waves of (16 FV) x (16 FR), both operands staged in LDS.
 constexpr int kBigWaves = 8;
 constexpr int kBigThreads = kBigWaves * kWave;
-constexpr int kWaveV = 128, kWaveR = 64;           // per-wave block
-constexpr int kFV = kWaveV / kLmTile, kFR = kWaveR / kLmTile;   // 8 x 4 fragments
 
-static_assert((kTV / kWaveV) * (kBigTR / kWaveR) == kBigWaves, "wave grid");
-
-// One K tile of both operands: 256 rows x 64 bf16 each = 2048 chunks of 16
-// bytes per operand, 4 per thread.
+// One K tile of both operands: 256 W rows and TR hidden rows x 64 bf16 =
+// 8 chunks of 16 bytes per row, 4 (W) and TR / 64 (hidden) per thread.
+template <int TR>
 struct BigStage {
-    u32x4 w[4], h[4];
+    u32x4 w[4], h[TR / 64];
 };
 
-__device__ __forceinline__ void big_load_stage(BigStage& s, const uint16_t* __restrict__ W,
-                                           const uint16_t* __restrict__ H, int v0, int r0, int k0,
-                                           int V, int R, int d) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = threadIdx.x + j * kBigThreads;      // chunk 0..2047
+template <int TR>
+__device__ __forceinline__ void big_load_stage(BigStage<TR>& s, const uint16_t* __restrict__ W,
+                                               const uint16_t* __restrict__ H, int v0, int r0,
+                                               int k0, int V, int R, int d) {
+    auto load = [&](const uint16_t* __restrict__ M, int base, int lim, int c) {
         const int row = c >> 3, col = (c & 7) * 8;      // 8 chunks per 64-element row
         const int k = k0 + col;
-        const int v = min(v0 + row, V - 1);             // past the end: a valid row, never stored
-        const int r = min(r0 + row, R - 1);
-        if (k < d) {
-            s.w[j] = *reinterpret_cast<const u32x4*>(W + (size_t)v * d + k);
-            s.h[j] = *reinterpret_cast<const u32x4*>(H + (size_t)r * d + k);
-        } else {
-            s.w[j] = u32x4{0u, 0u, 0u, 0u};
-            s.h[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
-__device__ __forceinline__ void big_store_stage(const BigStage& s, char* lw, char* lh) {
+        const int x = min(base + row, lim - 1);         // past the end: a valid row, never stored
+        return k < d ? *reinterpret_cast<const u32x4*>(M + (size_t)x * d + k) : u32x4{0u, 0u, 0u, 0u};
+    };
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = threadIdx.x + j * kBigThreads;
-        const int row = c >> 3, col = c & 7;
-        *reinterpret_cast<u32x4*>(lw + row * kRowBytes + col * 16) = s.w[j];
-        *reinterpret_cast<u32x4*>(lh + row * kRowBytes + col * 16) = s.h[j];
-    }
+    for (int j = 0; j < 4; ++j) s.w[j] = load(W, v0, V, threadIdx.x + j * kBigThreads);
+#pragma unroll
+    for (int j = 0; j < TR / 64; ++j) s.h[j] = load(H, r0, R, threadIdx.x + j * kBigThreads);
 }
 
+template <int TR>
+__device__ __forceinline__ void big_store_stage(const BigStage<TR>& s, char* lw, char* lh) {
+    auto store = [&](char* l, int c, const u32x4& v) {
+        *reinterpret_cast<u32x4*>(l + (c >> 3) * kRowBytes + (c & 7) * 16) = v;
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store(lw, threadIdx.x + j * kBigThreads, s.w[j]);
+#pragma unroll
+    for (int j = 0; j < TR / 64; ++j) store(lh, threadIdx.x + j * kBigThreads, s.h[j]);
+}
+
+template <int TR, int WV, int FV, int FR>
 __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
     float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
     int32_t* __restrict__ counters, int n_counters) {
-    // LDS: two stages of (W tile, hidden tile), each 256 rows x 144 bytes.
-    __shared__ __attribute__((aligned(16))) char lds[2][2][kTV * kRowBytes];
-    __shared__ float s_max[kTV / kWaveV][kBigTR];
-    __shared__ float s_sum[kTV / kWaveV][kBigTR];
-    __shared__ float s_av[kTV / kWaveV][kBigTR];
-    __shared__ int s_ai[kTV / kWaveV][kBigTR];
+    constexpr int kWaveV = FV * kLmTile, kWaveR = FR * kLmTile;
+    constexpr int WR = kBigWaves / WV;
+    static_assert(WV * kWaveV == kTV && WR * kWaveR == TR && TR % 64 == 0, "wave grid");
+    constexpr int kFV = FV, kFR = FR;
+    // LDS: two stages of the W tile (256 rows) and the hidden tile (TR rows),
+    // 144-byte rows.
+    __shared__ __attribute__((aligned(16))) char ldsw[2][kTV * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char ldsh[2][TR * kRowBytes];
+    __shared__ float s_max[WV][TR];
+    __shared__ float s_sum[WV][TR];
+    __shared__ float s_av[WV][TR];
+    __shared__ int s_ai[WV][TR];
 
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
         counters[i] = 0;
@@ -121,11 +122,11 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
     const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nblocks) return;          // padding blocks of the rounded-up grid
     const int vb = logical / nrb, rb = logical % nrb;
-    const int v0 = vb * kTV, r0 = rb * kBigTR;
+    const int v0 = vb * kTV, r0 = rb * TR;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wv = wave & 1, wr = wave >> 1;            // 2 (vocab) x 4 (rows) waves
+    const int wv = wave % WV, wr = wave / WV;          // WV (vocab) x WR (rows) waves
     const int r16 = lane & 15, kg = lane >> 4;
 
     f32x4 acc[kFV][kFR];
@@ -138,15 +139,15 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
     // K tiles from an offset of the block's own (see lmhead_mid_kernel).
     const int rot = (int)(((unsigned)vb * 2654435761u >> 16) % (unsigned)nk);
     auto ktile = [&](int kt) { const int t = kt + rot; return (t >= nk ? t - nk : t) * kTK; };
-    BigStage st;
-    big_load_stage(st, W, hidden, v0, r0, ktile(0), V, R, d);
-    big_store_stage(st, lds[0][0], lds[0][1]);
+    BigStage<TR> st;
+    big_load_stage<TR>(st, W, hidden, v0, r0, ktile(0), V, R, d);
+    big_store_stage<TR>(st, ldsw[0], ldsh[0]);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) big_load_stage(st, W, hidden, v0, r0, ktile(kt + 1), V, R, d);
-        const char* lw = lds[cur][0] + (wv * kWaveV + r16) * kRowBytes + kg * 16;
-        const char* lh = lds[cur][1] + (wr * kWaveR + r16) * kRowBytes + kg * 16;
+        if (kt + 1 < nk) big_load_stage<TR>(st, W, hidden, v0, r0, ktile(kt + 1), V, R, d);
+        const char* lw = ldsw[cur] + (wv * kWaveV + r16) * kRowBytes + kg * 16;
+        const char* lh = ldsh[cur] + (wr * kWaveR + r16) * kRowBytes + kg * 16;
 #pragma unroll
         for (int ks = 0; ks < kTK / 32; ++ks) {
             u32x4 fa[kFV], fb[kFR];
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
                         __builtin_bit_cast(bf16x8, fa[a]), __builtin_bit_cast(bf16x8, fb[b]),
                         acc[a][b], 0, 0, 0);
         }
-        if (kt + 1 < nk) big_store_stage(st, lds[cur ^ 1][0], lds[cur ^ 1][1]);
+        if (kt + 1 < nk) big_store_stage<TR>(st, ldsw[cur ^ 1], ldsh[cur ^ 1]);
         __syncthreads();
     }
 
@@ -227,12 +228,12 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
         if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; s_av[wv][rl] = av; s_ai[wv][rl] = ai; }
     }
     __syncthreads();
-    if (threadIdx.x < kBigTR && r0 + (int)threadIdx.x < R) {
+    if (threadIdx.x < TR && r0 + (int)threadIdx.x < R) {
         const int rl = threadIdx.x;
         float m = -INFINITY, s = 0.f, av = -INFINITY;
         int ai = -1;
 #pragma unroll
-        for (int w = 0; w < kTV / kWaveV; ++w) {
+        for (int w = 0; w < WV; ++w) {
             lse_merge(m, s, s_max[w][rl], s_sum[w][rl]);
             arg_merge(av, ai, s_av[w][rl], s_ai[w][rl]);
         }
@@ -611,12 +612,26 @@ hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R,
     if (R <= 128)
         return launch_shape<4, 8, 4, 1, 8>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
                                            NPs, counters, n_counters, stream);
+    // The row-block height that pads R least (ties to the taller block, whose
+    // W tile then serves more rows): R = 320 runs two blocks of 192 rows
+    // rather than two of 256, R = 1280 five of 256.
     const int nvb = lmhead_tiled_partials(V);
-    const int nrb = (R + kBigTR - 1) / kBigTR;
+    int TR = 256;
+    for (int tr : {192, 128})
+        if ((R + tr - 1) / tr * tr < (R + TR - 1) / TR * TR) TR = tr;
+    const int nrb = (R + TR - 1) / TR;
     const int nblocks = nvb * nrb;
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
-    lmhead_big_kernel<<<dim3(grid), dim3(kBigThreads), 0, stream>>>(
-        hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+    const dim3 g(grid), b(kBigThreads);
+    if (TR == 256)
+        lmhead_big_kernel<256, 2, 8, 4><<<g, b, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+    else if (TR == 192)
+        lmhead_big_kernel<192, 4, 4, 6><<<g, b, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+    else
+        lmhead_big_kernel<128, 4, 4, 4><<<g, b, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     return hipGetLastError();
 }
 
