@@ -71,6 +71,26 @@ def traffic_from_counters(cfg_name: str):
     return None
 
 
+def mfma_busy_from_counters(cfg_name: str):
+    """Counter-based MFMA busy fraction of the tiled LM-head GEMM.
+
+    From committed rocprofv3 runs (profiles/*_mfma_util.json: the
+    derived MfmaUtil counter, MFMA busy cycles over active cycles of every
+    SIMD) of the default mode of one workload each; None when there is no
+    summary for this workload or the kernel's sources have changed since.
+    """
+    import glob
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_mfma_util.json"))):
+        with open(path) as f:
+            c = json.load(f)
+        if c.get("workload") != cfg_name:
+            continue
+        if c.get("kernel_hash") != source_hash(c.get("kernel_sources", [])):
+            return None
+        return c.get("mfma_util_pct") / 100.0
+    return None
+
+
 def cpu_baseline(x: dict, budget_s: float = 20.0, greedy: bool = False) -> dict:
     """Time the fp64 oracle (as it stands) on the same inputs, on the host."""
     from threadpoolctl import threadpool_info
@@ -284,8 +304,8 @@ def main():
             step_bytes = perfmodel.step_bytes(B, g, d, V, int((n_host < g).sum()))
         # R <= 64 rows: the streaming kernel, one launch per 64 rows; more
         # rows: one launch of the pipelined 128-row GEMM (R <= 128) or of the
-        # 256 x 256 LDS-tiled GEMM (when their partials fit, as in every named
-        # workload).
+        # LDS-tiled GEMM of 256-entry x 128/192/256-row blocks (when their
+        # partials fit, as in every named workload).
         tiled = R > 64 and -(-V // 256) <= 1024
         passes = 1 if tiled else -(-R // 64)
         kernel = ("lmhead_mid_kernel" if R <= 128 else "lmhead_big_kernel") if tiled else "lmhead_kernel"
@@ -336,6 +356,7 @@ def main():
         "lmhead_ms_avg": statistics.mean(lm_ms), "lmhead_ms_median": statistics.median(lm_ms),
         "lmhead_launches_per_step": passes,
         "mfma_frac": flops / lm_avg_s / perfmodel.MI355X_BF16_DENSE_FLOPS,
+        "mfma_busy_frac_counters": mfma_busy_from_counters(cfg.name) if mode == "sample" else None,
         "roofline": roof,
     }
     if n_host is not None:

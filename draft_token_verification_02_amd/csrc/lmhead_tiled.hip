@@ -28,12 +28,14 @@
 // Staging only the small operand in LDS keeps LDS traffic low, and W never
 // waits behind the hidden tile's loads in the in-order vmcnt queue.
 //
-// R > 128 (lmhead_big_kernel): MFMA bound at R = 1280.  256 x 256 blocks,
-// 8 waves of 128 x 64 (8 x 4 fragments); both operands staged through
-// registers into LDS per 64-wide K tile (rows padded to 144 bytes so the
-// 16-byte fragment reads of 8 lanes hit distinct banks), one tile ahead.
-// The larger block halves the L2 traffic per flop of a 128-row block, which
-// is what bounds the many-row case.
+// R > 128 (lmhead_big_kernel): MFMA bound at R = 1280.  Blocks of 256 vocab
+// entries x TR rows, TR = 128, 192 or 256 -- whichever leaves the fewest
+// padded rows (R = 320 runs two 192-row blocks instead of two 256-row ones,
+// 4.8 rather than 7.2 padded MFMA columns per computed one) -- 8 waves each;
+// both operands staged through registers into LDS per 64-wide K tile (rows
+// padded to 144 bytes so the 16-byte fragment reads of 8 lanes hit distinct
+// banks), one tile ahead.  At R = 1280 the 256-row block halves the L2
+// traffic per flop of a 128-row block, which is what bounds that case.
 
 // Block order.  Workgroups are dispatched round-robin over the 8 XCDs; the
 // block index is remapped so that each XCD receives a contiguous run of the
