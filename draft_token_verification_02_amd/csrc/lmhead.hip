@@ -92,6 +92,36 @@ constexpr int kStageGroups = (32768 / (MT * kLmTile * T * kLmTile * 4)) > 0
 
 __device__ __forceinline__ bool vec_store_ok(int V) { return (V & 3) == 0; }
 
+// exp(x) for x <= 0 (or -inf) through the hardware exp2.
+__device__ __forceinline__ float exp2_scaled(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
+// DPP quad permutations: exchange with lane ^ 1 and with lane ^ 2.
+constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
+
+template <int CTRL>
+__device__ __forceinline__ float quad_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int quad_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// Merge this lane's softmax partial (m, s) and greedy candidate (av, ai)
+// with those of its partner lane in the quad.
+template <int CTRL>
+__device__ __forceinline__ void quad_merge(float& m, float& s, float& av, int& ai) {
+    const float m2 = quad_f32<CTRL>(m), s2 = quad_f32<CTRL>(s), av2 = quad_f32<CTRL>(av);
+    const int ai2 = quad_i32<CTRL>(ai);
+    const float nm = fmaxf(m, m2);
+    s = nm == -INFINITY ? 0.f : s * exp2_scaled(m - nm) + s2 * exp2_scaled(m2 - nm);
+    m = nm;
+    arg_merge(av, ai, av2, ai2);
+}
+
 template <int MT, int T, int U, bool FAST>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int row0, int rows,
@@ -195,20 +225,50 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     __shared__ __attribute__((aligned(16))) float stage[kLmWaves][MT * kLmTile][kSegPad];
     float (*st)[kSegPad] = stage[wave];
     int stage_first = gb, staged = 0;
+    // The stage is written as one flat run of 16-byte pieces over (row,
+    // vocab), kWave pieces per store instruction: each lane reads
+    // kFlushBatch pieces from LDS before storing any, so the LDS latency is
+    // paid once per batch rather than once per row, and walks its (row,
+    // piece) position by adding a fixed step -- no division per piece.
+    constexpr int kFlushBatch = 8;
     auto flush = [&]() {
         const int vbase = stage_first * T * kLmTile;
-        const int nvals = staged * T * kLmTile;
-        for (int rr = 0; rr < rows && rr < MT * kLmTile; ++rr) {
-            float* lrow = logits + (size_t)(row0 + rr) * V;
-            for (int j = lane * 4; j < nvals; j += kWave * 4) {
-                const int v = vbase + j;
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&st[rr][j]);
-                if (vec_store_ok(V) && v + 3 < V) {
-                    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(lrow + v));
-                } else {
+        const int per_row = staged * T * (kLmTile / 4);        // 16-byte pieces per row, >= 16
+        const int nrows = min(rows, MT * kLmTile);
+        const int dq = kWave / per_row, dr = kWave % per_row;  // the step, in rows + pieces
+        const bool whole = vec_store_ok(V) && vbase + per_row * 4 <= V;
+        int rr = lane / per_row, jp = lane % per_row;
+        while (rr < nrows) {
+            f32x4 x[kFlushBatch];
+            int ur[kFlushBatch], uj[kFlushBatch];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (v + i < V) lrow[v + i] = x[i];
+            for (int u = 0; u < kFlushBatch; ++u) {
+                ur[u] = rr;
+                uj[u] = jp * 4;
+                x[u] = *reinterpret_cast<const f32x4*>(&st[min(rr, nrows - 1)][jp * 4]);
+                rr += dq;
+                jp += dr;
+                if (jp >= per_row) { jp -= per_row; ++rr; }
+            }
+            if (whole) {                                       // no piece crosses V
+#pragma unroll
+                for (int u = 0; u < kFlushBatch; ++u)
+                    if (ur[u] < nrows)
+                        __builtin_nontemporal_store(
+                            x[u], reinterpret_cast<f32x4*>(logits + (size_t)(row0 + ur[u]) * V + vbase + uj[u]));
+            } else {
+#pragma unroll
+                for (int u = 0; u < kFlushBatch; ++u) {
+                    if (ur[u] >= nrows) continue;
+                    float* lrow = logits + (size_t)(row0 + ur[u]) * V;
+                    const int v = vbase + uj[u];
+                    if (vec_store_ok(V) && v + 3 < V) {
+                        __builtin_nontemporal_store(x[u], reinterpret_cast<f32x4*>(lrow + v));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (v + i < V) lrow[v + i] = x[u][i];
+                    }
                 }
             }
         }
@@ -336,43 +396,53 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
 
     if (keep_logits && staged > 0) flush();
 
-    // One partial per hidden row for the whole workgroup.
-    __shared__ float s_max[kLmWaves][MT * kLmTile];
-    __shared__ float s_sum[kLmWaves][MT * kLmTile];
-    __shared__ float s_av[kLmWaves][MT * kLmTile];
-    __shared__ int s_ai[kLmWaves][MT * kLmTile];
+    // One partial per hidden row for the whole workgroup.  Every lane's
+    // running partial (one per wave and k group: kSrc per row) goes to LDS as
+    // it is; then four adjacent lanes per row merge four partials each and
+    // combine across their quad with two DPP exchanges.  The end of the
+    // stream runs on few waves, so what counts is the length of the
+    // dependent instruction chain: the hardware exp2 (rescale factors are
+    // <= 1, relative error near 1e-7) and no LDS shuffles.
+    constexpr int kSrc = kLmWaves * 4;
+    constexpr int kSrcPad = kSrc + 4;                     // rows stay 16-byte aligned
+    static_assert(kSrc == 16, "four lanes per row, four partials per lane");
+    static_assert(MT * kLmTile * 4 <= kLmWaves * kWave, "a quad of lanes per row");
+    __shared__ __attribute__((aligned(16))) float s_max[MT * kLmTile][kSrcPad];
+    __shared__ __attribute__((aligned(16))) float s_sum[MT * kLmTile][kSrcPad];
+    __shared__ __attribute__((aligned(16))) float s_av[MT * kLmTile][kSrcPad];
+    __shared__ __attribute__((aligned(16))) int s_ai[MT * kLmTile][kSrcPad];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        float mm = run_m[m], ss = run_s[m], av = run_av[m];
-        int ai = run_ai[m];
-#pragma unroll
-        for (int off = 16; off < kWave; off <<= 1) {
-            const float m2 = __shfl_xor(mm, off), s2 = __shfl_xor(ss, off);
-            lse_merge(mm, ss, m2, s2);
-            const float av2 = __shfl_xor(av, off);
-            const int ai2 = __shfl_xor(ai, off);
-            arg_merge(av, ai, av2, ai2);
-        }
-        if (kg == 0) {
-            s_max[wave][m * kLmTile + r16] = mm;
-            s_sum[wave][m * kLmTile + r16] = ss;
-            s_av[wave][m * kLmTile + r16] = av;
-            s_ai[wave][m * kLmTile + r16] = ai;
-        }
+        const int c = wave * 4 + kg;
+        s_max[m * kLmTile + r16][c] = run_m[m];
+        s_sum[m * kLmTile + r16][c] = run_s[m];
+        s_av[m * kLmTile + r16][c] = run_av[m];
+        s_ai[m * kLmTile + r16][c] = run_ai[m];
     }
     __syncthreads();
-    if (threadIdx.x < MT * kLmTile && (int)threadIdx.x < rows) {
-        const int rr = threadIdx.x;
-        float m = -INFINITY, s = 0.f, av = -INFINITY;
-        int ai = -1;
-#pragma unroll
-        for (int w = 0; w < kLmWaves; ++w) {
-            lse_merge(m, s, s_max[w][rr], s_sum[w][rr]);
-            arg_merge(av, ai, s_av[w][rr], s_ai[w][rr]);
+    const int prow = threadIdx.x >> 2, pq = (threadIdx.x & 3) * 4;
+    if (prow < MT * kLmTile && prow < rows) {             // whole quads: a row's 4 lanes agree
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(&s_max[prow][pq]);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_sum[prow][pq]);
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&s_av[prow][pq]);
+        const int4 i4 = *reinterpret_cast<const int4*>(&s_ai[prow][pq]);
+        float m = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
+        float s = 0.f;
+        if (m != -INFINITY)
+            s = (sv[0] * exp2_scaled(mv[0] - m) + sv[1] * exp2_scaled(mv[1] - m)) +
+                (sv[2] * exp2_scaled(mv[2] - m) + sv[3] * exp2_scaled(mv[3] - m));
+        float av = a4[0], av1 = a4[2];
+        int ai = i4.x, ai1 = i4.z;
+        arg_merge(av, ai, a4[1], i4.y);
+        arg_merge(av1, ai1, a4[3], i4.w);
+        arg_merge(av, ai, av1, ai1);
+        quad_merge<kQuadXor1>(m, s, av, ai);
+        quad_merge<kQuadXor2>(m, s, av, ai);
+        if ((threadIdx.x & 3) == 0) {
+            part_max[(size_t)(row0 + prow) * NPs + blockIdx.x] = m;
+            part_sum[(size_t)(row0 + prow) * NPs + blockIdx.x] = s;
+            part_arg[(size_t)(row0 + prow) * NPs + blockIdx.x] = ai;
         }
-        part_max[(size_t)(row0 + rr) * NPs + blockIdx.x] = m;
-        part_sum[(size_t)(row0 + rr) * NPs + blockIdx.x] = s;
-        part_arg[(size_t)(row0 + rr) * NPs + blockIdx.x] = ai;
     }
 }
 
