@@ -18,12 +18,12 @@
 //
 // Launch shape.  The grid is persistent: one workgroup of kLmWaves waves per
 // compute unit (the register budget lets only one fit), and the vocabulary's
-// groups of T fragments are split evenly over all waves.  Each wave streams
-// its contiguous range as one sequence of (group, k-step) loads kept U steps
-// ahead of the MFMAs in a register ring; the ring runs across group
-// boundaries, so a group's epilogue (the fp32 logit stores and a running
-// (max, sum exp) per row) overlaps the next group's loads.  Few rows per
-// wave with a deep ring keeps each wave's HBM accesses on few DRAM pages.
+// groups of T fragments are dealt round-robin to all waves, so the grid
+// sweeps W front to back together.  Each wave streams its groups as one
+// sequence of (group, k-step) loads kept U steps ahead of the MFMAs in a
+// register ring; the ring runs across group boundaries, so a group's
+// epilogue (staging its fp32 logits and a running (max, sum exp) per row)
+// overlaps the next group's loads.
 // The workgroup reduces its running maxima and sums to one softmax partial
 // per row, so no later pass has to re-read the logits to normalise them, and
 // its greedy candidates to one (largest logit, lowest id) pair per row, from
@@ -50,11 +50,13 @@ namespace sv {
 namespace {
 
 // Fragments per wave and ring depth (k-steps in flight) by hidden-row
-// fragments MT, from a sweep on MI355X at d = 1536 and 4096: four fragments
-// four steps deep for one hidden fragment; more fragments, to share each
-// hidden-row load, and shallower rings as MT grows.
+// fragments MT, from sweeps on MI355X at d = 1536 and 4096 with the
+// round-robin group order: two fragments four steps deep for one hidden
+// fragment (one fragment loses once the 16 hidden rows are distinct: its
+// hidden loads match its W loads byte for byte); more fragments, to share
+// each hidden-row load, and shallower rings as MT grows.
 #ifndef SV_LM1_T
-#define SV_LM1_T 4
+#define SV_LM1_T 2
 #endif
 #ifndef SV_LM1_U
 #define SV_LM1_U 4
@@ -140,14 +142,18 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
         counters[i] = 0;
 
-    // This wave's groups of T fragments: an even split of all groups.
+    // This wave's groups of T fragments: wid, wid + nwaves, wid + 2 nwaves,
+    // ...  Dealt round-robin, the groups in flight across the GPU at any
+    // moment are neighbours, so the whole grid sweeps W from front to back
+    // in one narrow window -- the access order of a plain streaming read --
+    // rather than every wave walking a range of its own (measured: 138 ->
+    // 131 us at d = 1536, V = 262144 with one hidden fragment; 177 -> 172
+    // us at d = 4096).
     const int ntiles = (V + kLmTile - 1) / kLmTile;
     const int ngroups = (ntiles + T - 1) / T;
     const int nwaves = gridDim.x * kLmWaves;
     const int wid = blockIdx.x * kLmWaves + wave;
-    const int base = ngroups / nwaves, extra = ngroups % nwaves;
-    const int gb = wid * base + min(wid, extra);
-    const int ge = gb + base + (wid < extra ? 1 : 0);
+    const int gb = wid, ge = ngroups, gstep = nwaves;   // groups gb, gb + gstep, ... < ge
     const int nstep = (d + 31) / 32;
 
     const u32x4* hp[MT];
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         }
     };
     auto advance = [&]() {
-        if (++lk == nstep) { lk = 0; ++lg; if (lg < ge) set_rows(lg); }
+        if (++lk == nstep) { lk = 0; lg += gstep; if (lg < ge) set_rows(lg); }
     };
 
     f32x4 acc[T][MT];
@@ -214,12 +220,12 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     // nothing is staged or stored.
     const bool keep_logits = logits != nullptr;
 
-    // Logits are staged per wave in LDS (kStageGroups groups of T fragments,
+    // Logits are staged per wave in LDS (kStageGroups of the wave's groups,
     // rows padded by 16 bytes so the 16-byte writes of one fragment hit
-    // distinct banks) and written out as whole-row segments -- one 1 KB
-    // contiguous store per row and 256 vocab entries -- when the stage is
-    // full and at the end, instead of 64-byte pieces of 16 rows in the middle
-    // of the read stream.
+    // distinct banks) and written out when the stage is full and at the end:
+    // per row, one T*64-byte segment per staged group, instead of 64-byte
+    // pieces of 16 rows after every fragment.  Group k of the stage is the
+    // wave's group stage_first + k * gstep.
     constexpr int kSeg = kStageGroups<MT, T> * T * kLmTile;    // floats per staged row
     constexpr int kSegPad = kSeg + 4;
     __shared__ __attribute__((aligned(16))) float stage[kLmWaves][MT * kLmTile][kSegPad];
@@ -236,7 +242,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         const int per_row = staged * T * (kLmTile / 4);        // 16-byte pieces per row, >= 16
         const int nrows = min(rows, MT * kLmTile);
         const int dq = kWave / per_row, dr = kWave % per_row;  // the step, in rows + pieces
-        const bool whole = vec_store_ok(V) && vbase + per_row * 4 <= V;
+        const bool whole = vec_store_ok(V) && (stage_first + (staged - 1) * gstep + 1) * T * kLmTile <= V;
         int rr = lane / per_row, jp = lane % per_row;
         while (rr < nrows) {
             f32x4 x[kFlushBatch];
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
 #pragma unroll
             for (int u = 0; u < kFlushBatch; ++u) {
                 ur[u] = rr;
-                uj[u] = jp * 4;
+                uj[u] = (jp / (T * 4)) * gstep * T * kLmTile + (jp % (T * 4)) * 4;
                 x[u] = *reinterpret_cast<const f32x4*>(&st[min(rr, nrows - 1)][jp * 4]);
                 rr += dq;
                 jp += dr;
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 }
             }
         }
-        stage_first += staged;
+        stage_first += staged * gstep;
         staged = 0;
     };
     // Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment; its ids
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         }
         if (++staged == kStageGroups<MT, T>) {
             if (keep_logits) flush();
-            else { stage_first += staged; staged = 0; }
+            else { stage_first += staged * gstep; staged = 0; }
         }
     };
 
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 if (lk == nstep) lk = 0;
                 if (lcnt == nstep) {
                     lcnt = 0;
-                    ++lg;
+                    lg += gstep;
                     if (lg < ge) { set_rows(lg); lk = rot(lg); }
                 }
             };
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 }
                 next_block();
                 ck += U;
-                if (ck == nstep) { epilogue(cg); zero_acc(); ck = 0; ++cg; }
+                if (ck == nstep) { epilogue(cg); zero_acc(); ck = 0; cg += gstep; }
             }
         } else {
 #pragma unroll
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                         mma(u);
                         if (lg < ge) load(u);
                         advance();
-                        if (++ck == nstep) { epilogue(cg); zero_acc(); ck = 0; ++cg; }
+                        if (++ck == nstep) { epilogue(cg); zero_acc(); ck = 0; cg += gstep; }
                     }
                 }
             }
