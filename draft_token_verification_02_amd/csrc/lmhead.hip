@@ -29,6 +29,8 @@
 // its greedy candidates to one (largest logit, lowest id) pair per row, from
 // which greedy verification takes each row's argmax without the logits.
 
+#include <type_traits>
+
 #include "sv_common.h"
 
 #ifndef SV_LM_WG_PER_CU
@@ -283,36 +285,70 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     };
     // Lane holds D[vocab 4*kg + i][hidden row r16] of each fragment; its ids
     // rise with t and i, and with g, so a strict '>' keeps the first maximum.
+    // The epilogue runs between two k-steps of the stream, with the ring's
+    // loads in flight, on one wave per SIMD: short dependency chains matter.
+    // A group that lies inside V (all but possibly the last) takes the
+    // unchecked form: the group's max by a tree, the running sum's terms by
+    // the hardware exp2 (arguments <= 0, relative error near 1e-7) into four
+    // independent sums, and the first id of the group's max found by
+    // independent compares.
+    auto epilogue_row = [&](int m, int g, auto full_tag) {
+        constexpr bool kFull = decltype(full_tag)::value;
+        const int v0 = g * T * kLmTile + kg * 4;              // id of acc[0][m][0]
+        float mx = -INFINITY;
+        if (kFull) {
+            float mt[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                mt[t] = fmaxf(fmaxf(acc[t][m][0], acc[t][m][1]), fmaxf(acc[t][m][2], acc[t][m][3]));
+#pragma unroll
+            for (int h = T / 2; h >= 1; h >>= 1)
+#pragma unroll
+                for (int t = 0; t < h; ++t) mt[t] = fmaxf(mt[t], mt[t + h]);
+            mx = mt[0];
+            if (mx > run_av[m]) {
+                int id = 0;
+#pragma unroll
+                for (int t = T - 1; t >= 0; --t)
+#pragma unroll
+                    for (int e = 3; e >= 0; --e)
+                        id = acc[t][m][e] == mx ? v0 + t * kLmTile + e : id;
+                run_av[m] = mx;
+                run_ai[m] = id;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (v0 + t * kLmTile + e < V) {
+                        mx = fmaxf(mx, acc[t][m][e]);
+                        if (acc[t][m][e] > run_av[m]) { run_av[m] = acc[t][m][e]; run_ai[m] = v0 + t * kLmTile + e; }
+                    }
+        }
+        if (mx == -INFINITY) return;
+        const float nm = fmaxf(run_m[m], mx);
+        float sm[4] = {run_m[m] == -INFINITY ? 0.f : run_s[m] * exp2_scaled(run_m[m] - nm), 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (kFull || v0 + t * kLmTile + e < V) sm[e] += exp2_scaled(acc[t][m][e] - nm);
+        run_m[m] = nm;
+        run_s[m] = (sm[0] + sm[1]) + (sm[2] + sm[3]);
+    };
     auto epilogue = [&](int g) {
+        const bool full = (g + 1) * T * kLmTile <= V;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            float mx = -INFINITY;
+            if (keep_logits) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int v = (g * T + t) * kLmTile + kg * 4;
-                if (keep_logits)
+                for (int t = 0; t < T; ++t)
                     *reinterpret_cast<f32x4*>(&st[m * kLmTile + r16][(staged * T + t) * kLmTile + kg * 4]) =
                         acc[t][m];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (v + i < V) {
-                        mx = fmaxf(mx, acc[t][m][i]);
-                        if (acc[t][m][i] > run_av[m]) { run_av[m] = acc[t][m][i]; run_ai[m] = v + i; }
-                    }
             }
-            if (mx != -INFINITY) {
-                const float nm = fmaxf(run_m[m], mx);
-                float sm = run_s[m] * expf(run_m[m] - nm);   // exp(-inf) = 0 the first time
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const int v = (g * T + t) * kLmTile + kg * 4;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (v + i < V) sm += expf(acc[t][m][i] - nm);
-                }
-                run_m[m] = nm;
-                run_s[m] = sm;
-            }
+            if (full) epilogue_row(m, g, std::true_type{});
+            else epilogue_row(m, g, std::false_type{});
         }
         if (++staged == kStageGroups<MT, T>) {
             if (keep_logits) flush();
