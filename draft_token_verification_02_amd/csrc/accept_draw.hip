@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
     for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
     store_chunk_totals(tw, tp, cs, (size_t)b * NC + c);
     if (!FUSED) return;
-    if (!arrive_last(&counters[b], NC)) return;
+    if (!arrive_last(&counters[(size_t)b * kCounterStride], NC)) return;
     if (threadIdx.x >= kWave) return;          // the rest is one wave's
 
     // The sequence's last workgroup: outputs that depend on n only ...
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
         out_tokens[(size_t)b * g1 + n] = tok;
         n_accepted[b] = n;
         status[b] = flags | pflags;
-        counters[b] = 0;                       // ready for a repeated stage-2 call
+        counters[(size_t)b * kCounterStride] = 0;   // ready for a repeated stage-2 call
     }
 }
 

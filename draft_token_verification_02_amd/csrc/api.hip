@@ -74,12 +74,12 @@ sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* 
         e = sv::launch_lmhead_tiled(hidden, W, L.R, dims.d, dims.V, logits,
                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
                                     at<int32_t>(ws, L.part_arg), L.NPs,
-                                    at<int32_t>(ws, L.counters), dims.B, s);
+                                    at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
     else
         e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, logits,
                               at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
                               at<int32_t>(ws, L.part_arg), L.NPs, sv::lmhead_grid(dims.V),
-                              at<int32_t>(ws, L.counters), dims.B, s);
+                              at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 

@@ -34,6 +34,11 @@ constexpr int kDrawBlock = SV_DRAW_BLOCK;
 constexpr int kDrawChunk = 4096;                                                // tokens per chunk
 constexpr int kDrawPerThread = kDrawChunk / kDrawBlock;
 constexpr int kDrawWaves = kDrawBlock / kWave;
+// Each sequence's arrival counter sits on a 128-byte line of its own: the
+// counters take one device-scope atomic per draw workgroup, and atomics on
+// one line serialise (512 workgroups over 8 sequences sharing a line spent
+// ~7 us there).
+constexpr int kCounterStride = 32;
 static_assert(kDrawPerThread % 4 == 0, "whole 16-byte runs of tokens per thread");
 
 // LM-head workgroups worth launching for a vocabulary of V: at least one
@@ -92,7 +97,7 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     L.row_max = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
     L.row_sum = off;  off = align_up(off + (size_t)L.R * sizeof(float), 256);
     L.status = off;   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
-    L.counters = off; off = align_up(off + (size_t)B * sizeof(int32_t), 256);
+    L.counters = off; off = align_up(off + (size_t)B * kCounterStride * sizeof(int32_t), 256);
     L.csum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
     L.psum = off;     off = align_up(off + (size_t)B * L.NC * sizeof(double), 256);
     L.cwave = off;    off = align_up(off + (size_t)B * L.NC * kDrawWaves * sizeof(double), 256);

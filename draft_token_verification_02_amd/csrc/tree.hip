@@ -249,9 +249,9 @@ __global__ __launch_bounds__(kDrawBlock) void tree_round_kernel(
     const TreeState st = state[b];
     if (st.phase == kPhaseDone) return;
     tree_chunk_totals(st, tp, b, c, NC, a, cs);
-    if (!arrive_last(&counters[b], NC)) return;
+    if (!arrive_last(&counters[(size_t)b * kCounterStride], NC)) return;
     if (threadIdx.x >= kWave) return;          // the decision is one wave's
-    if (threadIdx.x == 0) counters[b] = 0;     // ready for the next round
+    if (threadIdx.x == 0) counters[(size_t)b * kCounterStride] = 0;   // ready for the next round
     tree_decide(st, tp, b, a, NC, cs, state, n_accepted, status);
 }
 
