@@ -259,10 +259,10 @@ __global__ __launch_bounds__(kWave) void pick_kernel(
 
 }  // namespace
 
-// Fused form up to 256 draw workgroups: stage 2 measured 8.7 us fused vs
-// 10.8 us split at B = 4 over 32 chunks, and 18.0 vs 11.0 us at 512
-// workgroups, where repeating the accept tests in every workgroup costs more
-// than two extra launches.
+// Fused form up to 256 draw workgroups: stage 2 measured 8.3 us fused vs
+// 10.8 us split at B = 4 over 32 chunks, and 15.6 vs 11.7 us at 512
+// workgroups (B = 8 over 64 chunks), where the workgroups' device-scope
+// releases and the repeated accept tests cost more than two extra launches.
 #ifndef SV_FUSE_MAX_GROUPS
 #define SV_FUSE_MAX_GROUPS 256
 #endif
