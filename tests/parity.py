@@ -23,6 +23,21 @@ LOGIT_RTOL = 2e-2
 P_ATOL = 1e-5
 
 
+def small_w_std(d: int) -> float:
+    """W's standard deviation for the small-shape parity cases.
+
+    The 1e-5 bar on p is met at the workloads' logit scale (W ~ N(0, 0.02^2):
+    logits of a few units), and fp32 accumulation of the logits moves p by
+    about p(1 - p) times the logit error, which grows with |logit|.  With W's
+    std fixed at 0.5 a d = 1536 case has logits up to ~93 and fp32 rounding
+    alone (~5e-5 on the logits) puts |dp| at 0.9e-5 or 1.5e-5 depending only on
+    the summation order.  Scaling W's std by 1/sqrt(d) keeps every small case
+    at a logit std of about 4 (as the d <= 64 cases have), where that rounding
+    stays well inside the bar.
+    """
+    return min(0.5, 4.0 / float(np.sqrt(d)))
+
+
 def to_device(x: dict, dev):
     """Upload through pinned host copies (one copy engine transfer each)."""
     import torch

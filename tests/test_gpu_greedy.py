@@ -80,7 +80,8 @@ def test_greedy_tiny():
 
 SMALL = [(3, 4, 200, 1000, 1), (2, 3, 1536, 5000, 2), (5, 2, 72, 777, 3), (1, 1, 8, 1, 4),
          (14, 4, 64, 4099, 5), (4, 8, 136, 300, 6), (2, 32, 40, 513, 7), (40, 7, 24, 65, 8),
-         (1, 4, 4096, 2048, 9), (300, 1, 16, 33, 10)]
+         (1, 4, 4096, 2048, 9), (300, 1, 16, 33, 10),
+         (4, 4, 256, 5000, 16), (8, 4, 128, 3001, 17)]   # several hidden fragments
 
 
 @pytest.mark.parametrize("B,gamma,d,V,seed", SMALL)

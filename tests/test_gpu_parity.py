@@ -70,6 +70,11 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (1, 3, 16, 262143, 13),    # 64 chunks (one window of chunk totals), ragged last chunk
     (1, 4, 32, 300000, 14),    # 74 chunks: the split draw and the pick's multi-window search
     (2, 2, 24, 270001, 15),
+    # several hidden fragments at small d
+    (4, 4, 256, 5000, 16),     # R = 20, two fragments, a partial last vocab group
+    (8, 4, 128, 3001, 17),     # R = 40, V % 4 != 0: per-element logit stores
+    (12, 4, 512, 2048, 18),    # R = 60, four fragments
+    (3, 7, 1536, 4096, 19),    # R = 24 at the Gemma-shaped d
 ]
 
 
@@ -77,7 +82,7 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
 def test_small_shapes_parity(B, gamma, d, V, seed):
     dev = _dev()
     _say(f"small B={B} gamma={gamma} d={d} V={V} seed={seed}")
-    x = I.custom(B, gamma, d, V, seed=seed, sigma=0.8)
+    x = I.custom(B, gamma, d, V, seed=seed, sigma=0.8, w_std=parity.small_w_std(d))
     rep = parity.compare(x, parity.run_gpu(x, dev))
     _report("small", rep)
 

@@ -82,7 +82,8 @@ SMALL = [  # (B, gamma, d, V, keep, seed): V ragged / several 4096-chunks, K % 4
 def test_sparse_q_small_parity(B, gamma, d, V, keep, seed):
     dev = _dev()
     _say(f"sparse-q small B={B} gamma={gamma} d={d} V={V} keep={keep} seed={seed}")
-    x = I.truncate_q(I.custom(B, gamma, d, V, seed=seed, sigma=0.8), keep, seed + 100)
+    x = I.truncate_q(I.custom(B, gamma, d, V, seed=seed, sigma=0.8, w_std=parity.small_w_std(d)), keep,
+                     seed + 100)
     ids, vals = I.to_sparse_q(x["q"], pad=3, dup=2, shuffle_seed=seed)
     rep = parity.compare(x, run_gpu_sparse(x, ids, vals, dev))
     _say("sparse-q small", rep)
