@@ -91,6 +91,30 @@ def mfma_busy_from_counters(cfg_name: str):
     return None
 
 
+def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
+    """Achievable HBM rate of a plain device copy: (read + write bytes) / time.
+
+    Context for the roofline: the fraction of 8 TB/s that a trivial streaming
+    kernel (torch's copy) reaches on this GPU, best of ``reps`` HIP-event-timed
+    copies of ``mib`` MiB, measured after the timed regions.
+    """
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    return 2 * n / best / 1e9
+
+
 def cpu_baseline(x: dict, budget_s: float = 20.0, greedy: bool = False) -> dict:
     """Time the fp64 oracle (as it stands) on the same inputs, on the host."""
     from threadpoolctl import threadpool_info
@@ -359,6 +383,7 @@ def main():
         "mfma_busy_frac_counters": mfma_busy_from_counters(cfg.name) if mode == "sample" else None,
         "roofline": roof,
     }
+    res["achievable_copy_GBps"] = copy_bandwidth(dev)
     if n_host is not None:
         res["emitted_tokens_per_s"] = float((n_host + 1).sum()) * K / elapsed
         res["n_accepted"] = n_host.tolist()[:16]
