@@ -17,9 +17,10 @@
 //                  one memory round trip each instead of a few long ones.
 //   topk_kernel    per row, the k largest cluster logits (ties to the lower
 //                  cluster id) by an exact 4-pass radix select on order-
-//                  preserving keys (two barriers per pass), then the chosen
-//                  clusters in ascending id and their members in the members
-//                  table's order: the row's K = k * M token ids.
+//                  preserving keys held in registers (1024 threads, one LDS
+//                  histogram, a DPP scan, two barriers per pass), then the
+//                  chosen clusters in ascending id and their members in the
+//                  members table's order: the row's K = k * M token ids.
 //   gather_kernel  token logits h . W[id] for the K ids of each row: W rows
 //                  gathered straight into the MFMA A operand (16 tokens per
 //                  fragment, 16 contiguous bytes per lane), the hidden row as
@@ -107,32 +108,27 @@ __global__ __launch_bounds__(kSplit * kWave) void scores_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup-wide integer scans in a fixed order.
-__device__ int block_inclusive_scan_int(int v, int* total) {
-    __shared__ int s_wave[kBlock / kWave];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    if (lane == kWave - 1) s_wave[wave] = v;
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) {
-        if (w < wave) before += s_wave[w];
-        all += s_wave[w];
-    }
-    __syncthreads();
-    *total = all;
-    return before + v;
-}
+// Top-k of the cluster logits, one 1024-thread workgroup per row.  Thread t
+// holds the keys of clusters t*P .. t*P+P-1 in registers (P = ceil(C/1024) <=
+// 8), so the chosen clusters come out in ascending id by thread order.
+constexpr int kTkBlock = 1024;
+constexpr int kTkWaves = kTkBlock / kWave;
+constexpr int kTkPer = (SV_HEAD_MAX_CLUSTERS + kTkBlock - 1) / kTkBlock;
 
-__device__ __forceinline__ int block_exclusive_scan_int(int v) {
-    int total;
-    return block_inclusive_scan_int(v, &total) - v;
+// Wave-wide inclusive sum on DPP lane moves (row_shr 1, 2, 4, 8, then the
+// row broadcasts 15 and 31); lanes without a source add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add_src(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int wave_scan_int(int v) {
+    v += dpp_add_src<0x111, 0xf>(v);
+    v += dpp_add_src<0x112, 0xf>(v);
+    v += dpp_add_src<0x114, 0xf>(v);
+    v += dpp_add_src<0x118, 0xf>(v);
+    v += dpp_add_src<0x142, 0xa>(v);
+    v += dpp_add_src<0x143, 0xc>(v);
+    return v;
 }
 
 // A key whose unsigned order is the float order (-0 and +0 equal, NaN lowest).
@@ -143,72 +139,51 @@ __device__ __forceinline__ unsigned order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(kBlock) void topk_kernel(
+__global__ __launch_bounds__(kTkBlock) void topk_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ members, int C, int M, int k,
     int V, int32_t* __restrict__ q_ids, int32_t* __restrict__ clusters) {
-    __shared__ unsigned s_key[SV_HEAD_MAX_CLUSTERS];
+    __shared__ int s_hist[256];
     __shared__ int s_sel[SV_HEAD_MAX_CLUSTERS];
-    __shared__ int s_hist[2][kBlock / kWave][256];   // per wave: scores of one size share their top digits
+    __shared__ int s_wsum[kTkWaves];
     __shared__ int s_digit, s_above;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int n = blockIdx.x;
     const float* row = scores + (size_t)n * C;
-    // Loads issued in batches of 8 per thread (one memory round trip each)
-    for (int c0 = 0; c0 < C; c0 += 8 * kBlock) {
-        float v[8];
+    const int P = (C + kTkBlock - 1) / kTkBlock;
+    const int cb = tid * P;
+    unsigned key[kTkPer];
+    bool valid[kTkPer];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int c = c0 + tid + u * kBlock;
-            v[u] = c < C ? row[c] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int c = c0 + tid + u * kBlock;
-            if (c < C) { s_key[c] = order_key(v[u]); s_sel[c] = -1; }
-        }
+    for (int j = 0; j < kTkPer; ++j) {
+        valid[j] = j < P && cb + j < C;
+        key[j] = valid[j] ? order_key(row[cb + j]) : 0u;
     }
-    const int wave = tid / kWave;
-#pragma unroll
-    for (int w = 0; w < kBlock / kWave; ++w) s_hist[0][w][tid] = 0;
+    if (tid < 256) s_hist[tid] = 0;
     __syncthreads();
 
-    // The k-th largest key, 8 bits at a time from the top: at each pass count
-    // the keys that match the digits found so far by their next digit, and
-    // take the digit where the count of keys at or above it reaches the
-    // number still needed.  The histograms alternate between two buffers (the
-    // next one is cleared during the pass), and one wave finds the digit:
-    // two barriers per pass.
+    // The k-th largest key, 8 bits at a time from the top: count the keys
+    // that match the digits found so far by their next digit (one LDS
+    // histogram); wave 0 scans the 256 counts from the highest digit (four
+    // per lane, a DPP scan), takes the digit where the count at or above it
+    // reaches the number still needed, and clears the histogram.  Two
+    // barriers per pass.
     unsigned prefix = 0u, pmask = 0u;
     int need = k;
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        int (*hist)[256] = s_hist[pass & 1];
-        for (int c = tid; c < C; c += kBlock) {
-            const unsigned key = s_key[c];
-            if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1);
-        }
 #pragma unroll
-        for (int w = 0; w < kBlock / kWave; ++w) s_hist[(pass + 1) & 1][w][tid] = 0;
+        for (int j = 0; j < kTkPer; ++j)
+            if (valid[j] && (key[j] & pmask) == prefix) atomicAdd(&s_hist[(key[j] >> shift) & 255u], 1);
         __syncthreads();
-        if (tid < kWave) {
-            // lane l holds digits 255 - 4l .. 252 - 4l, highest first
+        if (wave == 0) {
             int cnt[4], tot = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cnt[i] = 0;
-#pragma unroll
-                for (int w = 0; w < kBlock / kWave; ++w) cnt[i] += hist[w][255 - 4 * lane - i];
-                tot += cnt[i];
-            }
-            int incl = tot;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
-            const int before = incl - tot;               // keys with a higher digit
+            for (int i = 0; i < 4; ++i) { cnt[i] = s_hist[255 - 4 * lane - i]; tot += cnt[i]; }
+            const int incl = wave_scan_int(tot);
+            const int before = incl - tot;                 // keys with a higher digit
             if (before < need && incl >= need) {
                 int run = before;
 #pragma unroll
@@ -217,53 +192,61 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(
                     run += cnt[i];
                 }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_hist[255 - 4 * lane - i] = 0;
         }
         __syncthreads();
         prefix |= (unsigned)s_digit << shift;
         pmask |= 255u << shift;
         need -= s_above;
     }
+
     // Chosen: every key above the threshold, and the first `need` keys equal
-    // to it in cluster order.  Thread t owns clusters [t*per, (t+1)*per); one
-    // scan of (count above, count equal) packed in 16-bit halves places them.
-    const int per = (C + kBlock - 1) / kBlock;
-    const int cb = tid * per, ce = min(C, cb + per);
+    // to it in cluster order.  One exclusive scan of (count above, count
+    // equal), packed in 16-bit halves, places them in ascending id.
     int ngt = 0, neq = 0;
-    for (int c = cb; c < ce; ++c) {
-        const unsigned key = s_key[c];
-        ngt += key > prefix;
-        neq += key == prefix;
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+        ngt += valid[j] && key[j] > prefix;
+        neq += valid[j] && key[j] == prefix;
     }
-    const int packed = block_exclusive_scan_int((ngt << 16) | neq);
+    const int mine = (ngt << 16) | neq;
+    const int incl = wave_scan_int(mine);
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w)
+        if (w < wave) before += s_wsum[w];
+    const int packed = before + incl - mine;
     const int gt_before = packed >> 16, eq_before = packed & 0xffff;
     int pos = gt_before + min(eq_before, need), eqs = eq_before;
-    for (int c = cb; c < ce; ++c) {
-        const unsigned key = s_key[c];
-        const bool chosen = key > prefix || (key == prefix && eqs++ < need);
-        if (chosen) s_sel[pos++] = c;
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+        const bool chosen = valid[j] && (key[j] > prefix || (key[j] == prefix && eqs++ < need));
+        if (chosen) s_sel[pos++] = cb + j;
     }
     __syncthreads();
 
     if (clusters)
-        for (int j = tid; j < k; j += kBlock) clusters[(size_t)n * k + j] = s_sel[j];
+        for (int j = tid; j < k; j += kTkBlock) clusters[(size_t)n * k + j] = s_sel[j];
     const int K = k * M;
     int32_t* out = q_ids + (size_t)n * K;
-    // The members of the chosen clusters, gathered 8 per thread at a time.
-    for (int e0 = 0; e0 < K; e0 += 8 * kBlock) {
+    // The members of the chosen clusters, 8 per thread in flight at a time.
+    for (int e0 = 0; e0 < K; e0 += 8 * kTkBlock) {
         int id[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int e = e0 + tid + u * kBlock;
+            const int e = e0 + tid + u * kTkBlock;
             id[u] = -1;
             if (e < K) {
-                const int j = e / M, m = e - j * M;
-                const int c = s_sel[j];         // always a chosen cluster; -1 never read
-                if (c >= 0) id[u] = members[(size_t)c * M + m];
+                const int jj = e / M, m = e - jj * M;
+                id[u] = members[(size_t)s_sel[jj] * M + m];
             }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int e = e0 + tid + u * kBlock;
+            const int e = e0 + tid + u * kTkBlock;
             if (e < K) out[e] = id[u] >= 0 && id[u] < V ? id[u] : -1;
         }
     }
@@ -435,7 +418,7 @@ hipError_t launch_sparse_head(const uint16_t* h, const uint16_t* W, const uint16
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    topk_kernel<<<dim3(N), dim3(kBlock), 0, stream>>>(scores, members, C, M, k, V, q_ids, clusters);
+    topk_kernel<<<dim3(N), dim3(kTkBlock), 0, stream>>>(scores, members, C, M, k, V, q_ids, clusters);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     gather_kernel<<<dim3(L.G, N), dim3(kGWaves * kWave), 0, stream>>>(h, W, q_ids, K, d, tl, pmax,
