@@ -32,9 +32,9 @@
 // entries x TR rows, TR = 128, 192 or 256 -- whichever leaves the fewest
 // padded rows (R = 320 runs two 192-row blocks instead of two 256-row ones,
 // 4.8 rather than 7.2 padded MFMA columns per computed one) -- 8 waves each;
-// both operands staged through registers into LDS per 64-wide K tile (rows
-// padded to 144 bytes so the 16-byte fragment reads of 8 lanes hit distinct
-// banks), one tile ahead.  At R = 1280 the 256-row block halves the L2
+// both operands staged through registers into LDS per 64-wide K tile
+// (XOR-swizzled 128-byte rows, so fragment reads and stage writes hit
+// distinct banks), one tile ahead.  At R = 1280 the 256-row block halves the L2
 // traffic per flop of a 128-row block, which is what bounds that case.
 
 // Block order.  Workgroups are dispatched round-robin over the 8 XCDs; the
@@ -84,10 +84,18 @@ __device__ __forceinline__ void big_load_stage(BigStage<TR>& s, const uint16_t* 
     for (int j = 0; j < TR / 64; ++j) s.h[j] = load(H, r0, R, threadIdx.x + j * kBigThreads);
 }
 
+// LDS rows of 128 bytes with chunk g of row r in slot g ^ (r & 7): the
+// 16-byte fragment reads of 8 consecutive rows at one chunk, and the stage
+// writes of a row's 8 chunks, then hit distinct banks.  (Rows padded to 144
+// bytes instead left 37% of the LDS-active cycles as bank-conflict cycles in
+// rocprofv3's SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE at R = 1280.)
+constexpr int kBigRowBytes = kTK * 2;
+
 template <int TR>
 __device__ __forceinline__ void big_store_stage(const BigStage<TR>& s, char* lw, char* lh) {
     auto store = [&](char* l, int c, const u32x4& v) {
-        *reinterpret_cast<u32x4*>(l + (c >> 3) * kRowBytes + (c & 7) * 16) = v;
+        const int row = c >> 3;
+        *reinterpret_cast<u32x4*>(l + row * kBigRowBytes + ((c & 7) ^ (row & 7)) * 16) = v;
     };
 #pragma unroll
     for (int j = 0; j < 4; ++j) store(lw, threadIdx.x + j * kBigThreads, s.w[j]);
@@ -107,8 +115,8 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
     constexpr int kFV = FV, kFR = FR;
     // LDS: two stages of the W tile (256 rows) and the hidden tile (TR rows),
     // 144-byte rows.
-    __shared__ __attribute__((aligned(16))) char ldsw[2][kTV * kRowBytes];
-    __shared__ __attribute__((aligned(16))) char ldsh[2][TR * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char ldsw[2][kTV * kBigRowBytes];
+    __shared__ __attribute__((aligned(16))) char ldsh[2][TR * kBigRowBytes];
     __shared__ float s_max[WV][TR];
     __shared__ float s_sum[WV][TR];
     __shared__ float s_av[WV][TR];
@@ -148,17 +156,20 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < nk) big_load_stage<TR>(st, W, hidden, v0, r0, ktile(kt + 1), V, R, d);
-        const char* lw = ldsw[cur] + (wv * kWaveV + r16) * kRowBytes + kg * 16;
-        const char* lh = ldsh[cur] + (wr * kWaveR + r16) * kRowBytes + kg * 16;
+        // (fragment rows differ by multiples of 16, so every fragment of a
+        // lane shares the row's swizzle r16 & 7)
+        const char* lw = ldsw[cur] + (wv * kWaveV + r16) * kBigRowBytes;
+        const char* lh = ldsh[cur] + (wr * kWaveR + r16) * kBigRowBytes;
 #pragma unroll
         for (int ks = 0; ks < kTK / 32; ++ks) {
+            const int off = ((ks * 4 + kg) ^ (r16 & 7)) * 16;
             u32x4 fa[kFV], fb[kFR];
 #pragma unroll
             for (int a = 0; a < kFV; ++a)
-                fa[a] = *reinterpret_cast<const u32x4*>(lw + a * kLmTile * kRowBytes + ks * 64);
+                fa[a] = *reinterpret_cast<const u32x4*>(lw + a * kLmTile * kBigRowBytes + off);
 #pragma unroll
             for (int b = 0; b < kFR; ++b)
-                fb[b] = *reinterpret_cast<const u32x4*>(lh + b * kLmTile * kRowBytes + ks * 64);
+                fb[b] = *reinterpret_cast<const u32x4*>(lh + b * kLmTile * kBigRowBytes + off);
             // Every fragment read is issued before the first MFMA: left to
             // itself the compiler reuses one register quad for the A
             // fragments and waits out each read in turn (about 8% slower).
