@@ -309,7 +309,7 @@ __global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
     constexpr int NT = NW * kWave;                    // threads
     constexpr int CH = TR * (kTK / 8) / NT;           // 16-byte hidden chunks per thread per tile
     static_assert(kWaveV * WV == kTV && CH >= 1, "wave grid");
-    static_assert(!FAST || ((U == 2 || U == 4 || U == 8) && FR % 8 == 0), "ring depth and fragment groups");
+    static_assert(!FAST || ((U == 2 || U == 4 || U == 8) && (FR % 8 == 0 || FR < 8)), "ring depth and fragment groups");
 
     // FAST: four stages of TR x 128 bytes (swizzled), each its own array so
     // that the compiler can tell a stage being read from the stages the
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
         auto step_dma = [&](int st, int s, int slot) {
             const char* lh = stage(st) + brow + (s ? off1 : off0);
             // B fragments kFB at a time (register budget), each used by all FV
-            constexpr int kFB = 8;
+            constexpr int kFB = FR < 8 ? FR : 8;
 #pragma unroll
             for (int b0 = 0; b0 < FR; b0 += kFB) {
                 u32x4 fb[kFB];
@@ -622,6 +622,11 @@ hipError_t launch_shape(const uint16_t* hidden, const uint16_t* W, int R, int d,
 hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
                                float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                                int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
+    // 64 < R <= 96: 96-row blocks -- the hidden tile every k step copies is
+    // then 12 KB instead of 16 KB next to the same 32 KB of W.
+    if (R <= 96)
+        return launch_shape<4, 6, 4, 1, 8>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+                                           NPs, counters, n_counters, stream);
     if (R <= 128)
         return launch_shape<4, 8, 4, 1, 8>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
                                            NPs, counters, n_counters, stream);
