@@ -16,7 +16,9 @@
 //
 // 64 < R <= 128 (lmhead_mid_kernel): W-bandwidth bound.  A workgroup of four
 // waves computes a 256 (vocab) x 128 (row) block, each wave 64 vocab rows x
-// all 128 rows (4 x 8 fragments).  The operands travel differently:
+// all 128 rows (4 x 8 fragments); up to R = 96 the block is 96 rows (4 x 6
+// fragments), since the hidden tile copied every K tile takes its share of
+// the same load path as W.  The operands travel differently:
 //   * W goes from memory straight into the MFMA A registers -- each lane
 //     loads 16 contiguous bytes of one vocab row per 32-wide k step, the
 //     fragment layout itself -- kept 8 k-steps ahead in a register ring
