@@ -170,12 +170,18 @@ __global__ __launch_bounds__(kDrawBlock) void accept_kernel(
     }
 }
 
-// FUSED: every chunk workgroup runs the accept tests itself and the
-// sequence's last workgroup picks the token (few sequences: one launch).
-// Otherwise accept_kernel ran first, the workgroup reads n and the draw
-// row's normaliser it left, only writes its chunk totals, and pick_kernel
-// follows: the kernel boundary orders the totals before the pick.
-template <bool FUSED, bool SPARSE>
+// Three forms.  kDrawFused: every chunk workgroup runs the accept tests
+// itself and the sequence's last workgroup picks the token (few sequences:
+// one launch).  kDrawInline: every chunk workgroup runs the accept tests and
+// writes its chunk totals, chunk 0's workgroup writes the outputs that
+// depend on n only, and pick_kernel follows (two launches, no device-scope
+// arrival per workgroup).  kDrawSplit: accept_kernel ran first; the
+// workgroup reads n and the draw row's normaliser it left and writes its
+// chunk totals, and pick_kernel follows.  A kernel boundary orders the
+// totals before the pick in both two-launch forms.
+enum DrawForm { kDrawSplit = 0, kDrawFused = 1, kDrawInline = 2 };
+
+template <int FORM, bool SPARSE>
 __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
     const float* __restrict__ logits, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, int NP, int NPs, const int32_t* __restrict__ draft,
@@ -189,10 +195,12 @@ __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
     const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
     const int g1 = gamma + 1;
 
+    constexpr bool FUSED = FORM == kDrawFused;
+    constexpr bool ACCEPT = FORM != kDrawSplit;
     int flags = 0;
     int n;
     float M, S;
-    if (FUSED) {
+    if (ACCEPT) {
         n = accept_tests<SPARSE>(logits, part_max, part_sum, NP, NPs, b, gamma, V, draft, q,
                                  uniforms, r_m, r_s, &flags);
         M = r_m[n];
@@ -212,6 +220,18 @@ __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
 #pragma unroll
     for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
     store_chunk_totals(tw, tp, cs, (size_t)b * NC + c);
+    if (FORM == kDrawInline && c == 0) {       // the outputs that depend on n only
+        if (threadIdx.x < g1) {
+            const int i = threadIdx.x;
+            row_max[(size_t)b * g1 + i] = r_m[i];
+            row_sum[(size_t)b * g1 + i] = r_s[i];
+            if (i != n) out_tokens[(size_t)b * g1 + i] = i < n ? draft[(size_t)b * gamma + i] : -1;
+        }
+        if (threadIdx.x == 0) {
+            n_accepted[b] = n;
+            status[b] = flags;
+        }
+    }
     if (!FUSED) return;
     if (!arrive_last(&counters[(size_t)b * kCounterStride], NC)) return;
     if (threadIdx.x >= kWave) return;          // the rest is one wave's
@@ -266,6 +286,13 @@ __global__ __launch_bounds__(kWave) void pick_kernel(
 #ifndef SV_FUSE_MAX_GROUPS
 #define SV_FUSE_MAX_GROUPS 256
 #endif
+// Inline form from 257 to 1024 draw workgroups: 11.2 -> 9.6 us at 512
+// (B = 8 over 64 chunks, B = 16 over 32); at 2048 it measured 24.2 us against
+// 20.8 us split, where every workgroup repeating the accept tests costs more
+// than the accept launch.
+#ifndef SV_INLINE_MAX_GROUPS
+#define SV_INLINE_MAX_GROUPS 1024
+#endif
 
 namespace {
 
@@ -278,25 +305,37 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
                                 hipStream_t stream) {
     const unsigned groups = (unsigned)NC * (unsigned)B;
     // Few draw workgroups: fuse the accept tests into each and let the last
-    // one pick (one launch).  Many: accept once per sequence, chunk totals,
-    // then the pick -- three launches, no workgroup repeats the accept tests
-    // and none waits on a device-wide fence.
+    // one pick (one launch).  More: the accept tests in each workgroup, then
+    // the pick (two launches; no device-scope arrival per workgroup).  Many:
+    // accept once per sequence, chunk totals, then the pick -- three
+    // launches, no workgroup repeats the accept tests.
     if (groups <= SV_FUSE_MAX_GROUPS) {
-        draw_kernel<true, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+        draw_kernel<kDrawFused, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
             logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
             row_max, row_sum, out_tokens, n_accepted, status);
         return hipGetLastError();
     }
-    accept_kernel<SPARSE><<<dim3(B), dim3(kDrawBlock), 0, stream>>>(
-        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, row_max, row_sum,
-        out_tokens, n_accepted, status);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    draw_kernel<false, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
-        logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
-        row_max, row_sum, out_tokens, n_accepted, status);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    // (Sparse q stays split: repeating its id lookups in every workgroup
+    // measured slower, 172.3 -> 175.7 us per step at B = 8.)
+    if (!SPARSE && groups <= SV_INLINE_MAX_GROUPS) {
+        draw_kernel<kDrawInline, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+            logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
+            row_max, row_sum, out_tokens, n_accepted, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        accept_kernel<SPARSE><<<dim3(B), dim3(kDrawBlock), 0, stream>>>(
+            logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, row_max, row_sum,
+            out_tokens, n_accepted, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        draw_kernel<kDrawSplit, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+            logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
+            row_max, row_sum, out_tokens, n_accepted, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     pick_kernel<SPARSE><<<dim3(B), dim3(kWave), 0, stream>>>(logits, q, uniforms, gamma, V, NC, cs,
                                                             row_max, row_sum, out_tokens,
                                                             n_accepted, status);

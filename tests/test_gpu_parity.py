@@ -75,6 +75,8 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (8, 4, 128, 3001, 17),     # R = 40, V % 4 != 0: per-element logit stores
     (12, 4, 512, 2048, 18),    # R = 60, four fragments
     (3, 7, 1536, 4096, 19),    # R = 24 at the Gemma-shaped d
+    (16, 5, 512, 3000, 20),    # R = 96: the 128-row GEMM's 96-row blocks, pipelined path
+    (49, 1, 512, 2003, 21),    # R = 98: its 128-row blocks, V % 4 != 0
 ]
 
 
