@@ -279,14 +279,18 @@ __global__ __launch_bounds__(kWave) void pick_kernel(
 
 }  // namespace
 
-// Fused form up to 256 draw workgroups: stage 2 measured 8.3 us fused vs
-// 10.8 us split at B = 4 over 32 chunks, and 15.6 vs 11.7 us at 512
-// workgroups (B = 8 over 64 chunks), where the workgroups' device-scope
-// releases and the repeated accept tests cost more than two extra launches.
+// Fused form up to 64 draw workgroups: stage 2 measured 7.6 us fused vs
+// 7.7 us inline at B = 1 over 64 chunks, 8.4 vs 8.0 us at B = 4 over 32
+// chunks (and 10.8 us split), and 15.6 vs 9.6 us at 512 workgroups, where the
+// workgroups' device-scope releases cost more than the pick's extra launch.
 #ifndef SV_FUSE_MAX_GROUPS
-#define SV_FUSE_MAX_GROUPS 256
+#define SV_FUSE_MAX_GROUPS 64
 #endif
-// Inline form from 257 to 1024 draw workgroups: 11.2 -> 9.6 us at 512
+// Sparse q has no inline form (below), so it stays fused up to 256.
+#ifndef SV_FUSE_MAX_GROUPS_SPARSE
+#define SV_FUSE_MAX_GROUPS_SPARSE 256
+#endif
+// Inline form from 65 to 1024 draw workgroups: 11.2 -> 9.6 us at 512
 // (B = 8 over 64 chunks, B = 16 over 32); at 2048 it measured 24.2 us against
 // 20.8 us split, where every workgroup repeating the accept tests costs more
 // than the accept launch.
@@ -309,7 +313,7 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
     // the pick (two launches; no device-scope arrival per workgroup).  Many:
     // accept once per sequence, chunk totals, then the pick -- three
     // launches, no workgroup repeats the accept tests.
-    if (groups <= SV_FUSE_MAX_GROUPS) {
+    if (groups <= (SPARSE ? SV_FUSE_MAX_GROUPS_SPARSE : SV_FUSE_MAX_GROUPS)) {
         draw_kernel<kDrawFused, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
             logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
             row_max, row_sum, out_tokens, n_accepted, status);
