@@ -151,7 +151,7 @@ def main():
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the verification step here runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
