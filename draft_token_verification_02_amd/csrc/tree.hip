@@ -65,26 +65,70 @@ struct TreeArgs {
     int V;
     int32_t* out_tokens;       // [B][D+1]
     int32_t* path_nodes;       // [B][D] or null
+    int8_t parent_row[SV_MAX_TREE_NODES];   // per node: its parent's row (0 = root)
 };
 
 __device__ __forceinline__ size_t grow(int b, const TreeTopo& tp, int row) {
     return (size_t)b * (tp.T + 1) + row;
 }
 
+// What the walk reads at node t: its token x, its uniform r, and p and q of x
+// at its parent's row.  One wave gathers them for every node at once, lane t
+// taking node t (at most 64 nodes), so that the walk -- one thread -- reads
+// LDS instead of making two dependent trips to memory per node.  In two
+// parts: node_keys issues the loads that need only the topology (token,
+// uniform, the parent row's normaliser), node_table the gathers at the token.
+struct NodeVal {
+    float px, qx, r;
+    int x;
+};
+
+struct NodeKeys {
+    int x, prow;
+    float r, m, s;
+};
+
+__device__ __forceinline__ NodeKeys node_keys(const TreeTopo& tp, int b, const TreeArgs& a,
+                                              const float* rmax, const float* rsum) {
+    const int lane = threadIdx.x & (kWave - 1);
+    NodeKeys k{-1, 0, 0.f, 0.f, 0.f};
+    if (lane < tp.T) {
+        k.prow = a.parent_row[lane];
+        k.x = a.tokens[(size_t)b * tp.T + lane];
+        k.r = a.uniforms[(size_t)b * (tp.T + 1) + lane];
+        k.m = rmax[k.prow];
+        k.s = rsum[k.prow];
+    }
+    return k;
+}
+
+__device__ __forceinline__ void node_table(const NodeKeys& k, const TreeTopo& tp, int b,
+                                           const TreeArgs& a, NodeVal* s_node) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (lane >= tp.T) return;
+    NodeVal v{0.f, 0.f, k.r, k.x};
+    if (k.x >= 0 && k.x < a.V) {
+        const float lx = a.logits[grow(b, tp, k.prow) * a.V + k.x];
+        v.qx = a.q[((size_t)b * tp.P + tp.qslot[k.prow]) * a.V + k.x];
+        v.px = target_prob(lx, k.m, k.s);
+    }
+    s_node[lane] = v;
+}
+
 // Runs the walk of sequence b from its state until it needs a sum (or a
-// draw).  S is the sum for a pending test of rank j >= 1.  One thread.
+// draw).  S is the sum for a pending test of rank j >= 1.  One thread, after
+// its wave has filled s_node (node_keys, node_table).
 __device__ void tree_advance(TreeState& st, double S, const TreeTopo& tp, int b, const TreeArgs& a,
-                             const float* rmax, const float* rsum) {
-    const int T = tp.T;
+                             const NodeVal* s_node) {
     for (;;) {
         const int t = st.kid;
-        const int x = a.tokens[(size_t)b * T + t];
-        const float r = a.uniforms[(size_t)b * (T + 1) + t];
-        const size_t gr = grow(b, tp, st.row);
+        const NodeVal nv = s_node[t];          // node t's values at its parent, st.row
+        const int x = nv.x;
+        const float r = nv.r;
         bool keep = false;
         if (x >= 0 && x < a.V) {
-            const float px = target_prob(a.logits[gr * a.V + x], rmax[st.row], rsum[st.row]);
-            const float qx = a.q[((size_t)b * tp.P + tp.qslot[st.row]) * a.V + x];
+            const float px = nv.px;
+            const float qx = nv.qx;
             if (st.j == 0) {
                 keep = r * qx <= px;
             } else {
@@ -152,6 +196,9 @@ __global__ __launch_bounds__(kDrawBlock) void tree_init_kernel(
         row_max[(size_t)b * T1 + i] = r_m[i];
         row_sum[(size_t)b * T1 + i] = r_s[i];
     }
+    if (threadIdx.x >= kWave) return;
+    __shared__ NodeVal s_node[SV_MAX_TREE_NODES];
+    node_table(node_keys(tp, b, a, r_m, r_s), tp, b, a, s_node);
     if (threadIdx.x == 0) {
         TreeState st;
         st.c = 0.0;
@@ -160,7 +207,7 @@ __global__ __launch_bounds__(kDrawBlock) void tree_init_kernel(
         st.j = 0;
         st.depth = 0;
         st.flags = 0;
-        tree_advance(st, 1.0, tp, b, a, r_m, r_s);
+        tree_advance(st, 1.0, tp, b, a, s_node);
         state[b] = st;
         n_accepted[b] = st.depth;
         status[b] = st.flags;
@@ -191,15 +238,18 @@ __device__ void tree_decide(TreeState st, const TreeTopo& tp, int b, const TreeA
                             int32_t* __restrict__ n_accepted, int32_t* __restrict__ status) {
     const int lane = threadIdx.x & (kWave - 1);
     const DrawRow d = tree_draw_row(st, tp, b, a);
+    __shared__ NodeVal s_node[SV_MAX_TREE_NODES];
+    const size_t g0 = grow(b, tp, 0);
+    const NodeKeys keys = node_keys(tp, b, a, a.row_max + g0, a.row_sum + g0);
     // S in the association the pick uses; every lane has it, so every lane
     // takes the same branch.
     const double S = chunk_total_sum(cs.csum + (size_t)b * NC, NC);
     bool draw = st.phase != kPhaseSum;
     if (!draw && !(S > 0.0 && S < INFINITY)) draw = true;   // no residual mass: the pick falls back to p
     if (!draw) {
+        node_table(keys, tp, b, a, s_node);
         if (lane == 0) {
-            const size_t g0 = grow(b, tp, 0);
-            tree_advance(st, S, tp, b, a, a.row_max + g0, a.row_sum + g0);
+            tree_advance(st, S, tp, b, a, s_node);
             state[b] = st;
             n_accepted[b] = st.depth;
             status[b] = st.flags;
@@ -267,7 +317,9 @@ hipError_t launch_tree(const float* logits, const float* part_max, const float* 
                        const ChunkSums& cs, float* row_max, float* row_sum, void* state,
                        int32_t* counters, int32_t* out_tokens, int32_t* n_accepted,
                        int32_t* path_nodes, int32_t* status, hipStream_t stream) {
-    TreeArgs a{logits, row_max, row_sum, tokens, q, uniforms, V, out_tokens, path_nodes};
+    TreeArgs a{logits, row_max, row_sum, tokens, q, uniforms, V, out_tokens, path_nodes, {}};
+    for (int row = 0; row <= tp.T; ++row)
+        for (int k = tp.first_child[row]; k >= 0; k = tp.next_sibling[k]) a.parent_row[k] = (int8_t)row;
     TreeState* st = static_cast<TreeState*>(state);
     tree_init_kernel<<<dim3(B), dim3(kDrawBlock), 0, stream>>>(part_max, part_sum, NP, NPs, tp, a,
                                                           row_max, row_sum, st, n_accepted,
