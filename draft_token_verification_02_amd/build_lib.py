@@ -11,6 +11,8 @@ SOURCES = ["lmhead.hip", "lmhead_tiled.hip", "accept_draw.hip", "greedy.hip", "s
 OUT = os.path.join(HERE, "libspecverify.so")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+         # every symbol resolved at link time (a missing kernel stub fails the build)
+         "-Wl,-z,defs",
          # keep packed fp32 instructions out of the generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

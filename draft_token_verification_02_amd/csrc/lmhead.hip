@@ -96,11 +96,6 @@ constexpr int kStageGroups = (32768 / (MT * kLmTile * T * kLmTile * 4)) > 0
 
 __device__ __forceinline__ bool vec_store_ok(int V) { return (V & 3) == 0; }
 
-// exp(x) for x <= 0 (or -inf) through the hardware exp2.
-__device__ __forceinline__ float exp2_scaled(float x) {
-    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
-}
-
 // DPP quad permutations: exchange with lane ^ 1 and with lane ^ 2.
 constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
 constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);

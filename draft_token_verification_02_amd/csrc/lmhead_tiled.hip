@@ -58,193 +58,327 @@ constexpr int kRowBytes = kTK * 2 + 16;            // padded LDS row: 144 bytes
 constexpr int kXcds = 8;
 
 // ---------------------------------------------------------------------------
-// R > 128: 256 x TR blocks (TR = 128, 192 or 256 rows, whichever pads R
-// least), 8 waves of (16 FV) x (16 FR), both operands staged in LDS.
-constexpr int kBigWaves = 8;
-constexpr int kBigThreads = kBigWaves * kWave;
+// R > 128: blocks of 256 vocab rows x TR = 64 FR hidden rows, eight waves in
+// a 2 (vocab) x 4 (rows) grid, each 128 vocab rows x 16 FR hidden rows
+// (8 x FR fragments).  Both operands go from memory straight into LDS
+// (global_load_lds_dwordx4: 16 bytes per lane, no registers on the way)
+// through a ring of S stages of one 32-wide k step each.
+//
+// Ping-pong.  Waves 0-3 (group A) and 4-7 (group B) share the SIMDs, one of
+// each per SIMD, and take turns: while one group issues its MFMAs for a k
+// step the other reads its next fragments from LDS, and two barriers per k
+// step (X, Y) swap the roles, so a SIMD's matrix unit always has a wave with
+// operands ready feeding it.  Each wave issues its share of the ring's
+// copies between its own MFMAs (one after each of the first fragment rows):
+// a copy that stalls in the memory pipeline then holds up only a wave whose
+// MFMAs already keep the matrix unit busy.  Per k step t:
+//   A: MFMAs(t) + copies of t+S-1 | wait own copies of t+1 | X | read frags(t+1) | Y
+//   B: read frags(t) | wait own copies of t+1 | X | MFMAs(t) + copies of t+S-1 | Y
+// Stage u % S holds step u.  Before X_t every wave has waited for its copies
+// of step t+1, so after X_t the stage of t+1 is whole (A reads it in Q_t, B
+// in P_{t+1}).  The copies of step t+S-1 go to stage (t-1) % S, which both
+// groups finished reading before step t began (A in Q_{t-2}, waited before
+// Y_{t-2}; B in P_{t-1}, waited before X_{t-1}).  Measured at R = 1280,
+// d = 4096 (per k step, s_memtime in a probe build): 40 MFMAs take ~680
+// cycles, a group's 13 fragment reads ~300-480.
+//
+// Stage layout: the 256 W rows, then the TR hidden rows, 64 bytes (32 bf16)
+// each; chunk g of row r sits in slot g ^ ((r >> 1) & 3), which rocprofv3's
+// SQ_LDS_BANK_CONFLICT counts as conflict-free for the fragment reads on
+// gfx950 (g ^ ((r >> 2) & 3) counted conflicts on half the active cycles).
+// A copy instruction writes 1 KB of the stage (lane i to byte 16 i), so each
+// lane loads the global chunk that belongs at its slot.
+constexpr int kBigK = 32;                          // k per stage: one MFMA k step
+constexpr int kBigRowBytes = kBigK * 2;            // 64
+constexpr int kBigWV = 2, kBigWR = 4, kBigFV = 8;  // wave grid and vocab fragments per wave
+constexpr int kBigNW = kBigWV * kBigWR;            // 8 waves
+constexpr int kBigNT = kBigNW * kWave;
 
-// One K tile of both operands: 256 W rows and TR hidden rows x 64 bf16 =
-// 8 chunks of 16 bytes per row, 4 (W) and TR / 64 (hidden) per thread.
-template <int TR>
-struct BigStage {
-    u32x4 w[4], h[TR / 64];
+template <int FR>
+struct BigCfg {
+    static constexpr int TV = kBigWV * kBigFV * kLmTile;        // 256 vocab rows per block
+    static constexpr int TR = kBigWR * FR * kLmTile;            // hidden rows per block
+    static constexpr int kStageBytes = (TV + TR) * kBigRowBytes;
+    static constexpr int NI = (TV + TR) * (kBigRowBytes / 16) / kWave;   // 1 KB copies per stage
+    static constexpr int NIW = (NI + kBigNW - 1) / kBigNW;               // per wave and stage
+    static_assert((TV + TR) % 16 == 0, "whole 1 KB copies");
 };
 
-template <int TR>
-__device__ __forceinline__ void big_load_stage(BigStage<TR>& s, const uint16_t* __restrict__ W,
-                                               const uint16_t* __restrict__ H, int v0, int r0,
-                                               int k0, int V, int R, int d) {
-    auto load = [&](const uint16_t* __restrict__ M, int base, int lim, int c) {
-        const int row = c >> 3, col = (c & 7) * 8;      // 8 chunks per 64-element row
-        const int k = k0 + col;
-        const int x = min(base + row, lim - 1);         // past the end: a valid row, never stored
-        return k < d ? *reinterpret_cast<const u32x4*>(M + (size_t)x * d + k) : u32x4{0u, 0u, 0u, 0u};
-    };
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s.w[j] = load(W, v0, V, threadIdx.x + j * kBigThreads);
-#pragma unroll
-    for (int j = 0; j < TR / 64; ++j) s.h[j] = load(H, r0, R, threadIdx.x + j * kBigThreads);
+// vmcnt helper (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most N vector-memory operations of this wave
+// are outstanding, leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// lgkmcnt(0): every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-// LDS rows of 128 bytes with chunk g of row r in slot g ^ (r & 7): the
-// 16-byte fragment reads of 8 consecutive rows at one chunk, and the stage
-// writes of a row's 8 chunks, then hit distinct banks.  (Rows padded to 144
-// bytes instead left 37% of the LDS-active cycles as bank-conflict cycles in
-// rocprofv3's SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE at R = 1280.)
-constexpr int kBigRowBytes = kTK * 2;
-
-template <int TR>
-__device__ __forceinline__ void big_store_stage(const BigStage<TR>& s, char* lw, char* lh) {
-    auto store = [&](char* l, int c, const u32x4& v) {
-        const int row = c >> 3;
-        *reinterpret_cast<u32x4*>(l + row * kBigRowBytes + ((c & 7) ^ (row & 7)) * 16) = v;
-    };
-#pragma unroll
-    for (int j = 0; j < 4; ++j) store(lw, threadIdx.x + j * kBigThreads, s.w[j]);
-#pragma unroll
-    for (int j = 0; j < TR / 64; ++j) store(lh, threadIdx.x + j * kBigThreads, s.h[j]);
-}
-
-template <int TR, int WV, int FV, int FR>
-__global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
+template <int FR, int S>
+__global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
     float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
     int32_t* __restrict__ counters, int n_counters) {
-    constexpr int kWaveV = FV * kLmTile, kWaveR = FR * kLmTile;
-    constexpr int WR = kBigWaves / WV;
-    static_assert(WV * kWaveV == kTV && WR * kWaveR == TR && TR % 64 == 0, "wave grid");
-    constexpr int kFV = FV, kFR = FR;
-    // LDS: two stages of the W tile (256 rows) and the hidden tile (TR rows),
-    // 144-byte rows.
-    __shared__ __attribute__((aligned(16))) char ldsw[2][kTV * kBigRowBytes];
-    __shared__ __attribute__((aligned(16))) char ldsh[2][TR * kBigRowBytes];
+    using C = BigCfg<FR>;
+    constexpr int TV = C::TV, TR = C::TR, NI = C::NI, NIW = C::NIW;
+    constexpr int WV = kBigWV, FV = kBigFV, NW = kBigNW;
+    static_assert(TV == kTV, "256 vocab rows per block: one softmax partial column each");
+    static_assert(S == 4, "ring depth");
+    // One array per stage, so that the compiler can tell the stage a
+    // fragment read uses from the stages copies are filling (with a single
+    // array it waits for every copy in flight before each read).
+    __shared__ __attribute__((aligned(1024))) char st0[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st1[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st2[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char st3[C::kStageBytes];
     __shared__ float s_max[WV][TR];
     __shared__ float s_sum[WV][TR];
     __shared__ float s_av[WV][TR];
     __shared__ int s_ai[WV][TR];
 
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counters; i += gridDim.x * blockDim.x)
-        counters[i] = 0;
-
     // XCD-aware block order: hardware block b runs on XCD b % 8; give each XCD
-    // a contiguous run of logical blocks, row blocks fastest.
+    // a contiguous run of logical blocks, row blocks fastest, so the row
+    // blocks sharing a W tile run together and take it from one L2.
     const int nblocks = nvb * nrb;
     const int per_xcd = (nblocks + kXcds - 1) / kXcds;
     const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nblocks) return;          // padding blocks of the rounded-up grid
     const int vb = logical / nrb, rb = logical % nrb;
-    const int v0 = vb * kTV, r0 = rb * TR;
+    const int v0 = vb * TV, r0 = rb * TR;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wv = wave % WV, wr = wave / WV;          // WV (vocab) x WR (rows) waves
+    const int wv = wave % WV, wr = wave / WV;           // group A: wr 0-1, group B: wr 2-3
+    const bool group_b = wave >= NW / 2;
     const int r16 = lane & 15, kg = lane >> 4;
 
-    f32x4 acc[kFV][kFR];
+    // This wave's copies: instruction j = wave + m * NW of the stage covers
+    // chunks 64 j .. 64 j + 63, lane i chunk 64 j + i: row c / 4, slot c % 4,
+    // holding k-chunk g = slot ^ ((row >> 1) & 3) of that row.  Rows past V
+    // (or R) copy the last valid row; their results are never stored.  When
+    // NI is not a multiple of NW a wave's last j may pass NI: it repeats its
+    // previous copy (same bytes to the same place), so every wave issues NIW
+    // copies per step and the vmcnt accounting is the same on every wave.
+    const uint16_t* src[NIW];
+    int dst[NIW];
+    // row = 16 j + lane / 4 with 16 j a multiple of 8, so (row >> 1) & 3 = (lane >> 3) & 3
+    const int goff = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
 #pragma unroll
-    for (int a = 0; a < kFV; ++a)
-#pragma unroll
-        for (int b = 0; b < kFR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = (d + kTK - 1) / kTK;
-    // K tiles from an offset of the block's own (see lmhead_mid_kernel).
-    const int rot = (int)(((unsigned)vb * 2654435761u >> 16) % (unsigned)nk);
-    auto ktile = [&](int kt) { const int t = kt + rot; return (t >= nk ? t - nk : t) * kTK; };
-    BigStage<TR> st;
-    big_load_stage<TR>(st, W, hidden, v0, r0, ktile(0), V, R, d);
-    big_store_stage<TR>(st, ldsw[0], ldsh[0]);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) big_load_stage<TR>(st, W, hidden, v0, r0, ktile(kt + 1), V, R, d);
-        // (fragment rows differ by multiples of 16, so every fragment of a
-        // lane shares the row's swizzle r16 & 7)
-        const char* lw = ldsw[cur] + (wv * kWaveV + r16) * kBigRowBytes;
-        const char* lh = ldsh[cur] + (wr * kWaveR + r16) * kBigRowBytes;
-#pragma unroll
-        for (int ks = 0; ks < kTK / 32; ++ks) {
-            const int off = ((ks * 4 + kg) ^ (r16 & 7)) * 16;
-            u32x4 fa[kFV], fb[kFR];
-#pragma unroll
-            for (int a = 0; a < kFV; ++a)
-                fa[a] = *reinterpret_cast<const u32x4*>(lw + a * kLmTile * kBigRowBytes + off);
-#pragma unroll
-            for (int b = 0; b < kFR; ++b)
-                fb[b] = *reinterpret_cast<const u32x4*>(lh + b * kLmTile * kBigRowBytes + off);
-            // Every fragment read is issued before the first MFMA: left to
-            // itself the compiler reuses one register quad for the A
-            // fragments and waits out each read in turn (about 8% slower).
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int a = 0; a < kFV; ++a)
-#pragma unroll
-                for (int b = 0; b < kFR; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, fa[a]), __builtin_bit_cast(bf16x8, fb[b]),
-                        acc[a][b], 0, 0, 0);
-        }
-        if (kt + 1 < nk) big_store_stage<TR>(st, ldsw[cur ^ 1], ldsh[cur ^ 1]);
-        __syncthreads();
+    for (int m = 0; m < NIW; ++m) {
+        const int j = wave + m * NW < NI ? wave + m * NW : wave + (m - 1) * NW;
+        const int row = j * 16 + (lane >> 2);
+        src[m] = (row < TV ? W + (size_t)min(v0 + row, V - 1) * d
+                           : hidden + (size_t)min(r0 + row - TV, R - 1) * d) + goff;
+        dst[m] = j * 1024;
     }
 
-    // Epilogue: lane holds D[vocab 4*kg + i][row r16] of each fragment; its
-    // ids rise with a and i, so a strict '>' keeps the first maximum.  No
-    // logits buffer: only the partials are written.
-    const bool vec_store = (V & 3) == 0;
+    const int nk = (d + kBigK - 1) / kBigK;
+    const bool ragged = d % kBigK != 0;       // the last step has chunks past the end of a row
+    auto stage = [&](int s) -> char* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
+    // Copies of step t (t >= nk: a repeat of the last step, into a stage no
+    // step reads again, so that every step issues the same copies).  A chunk
+    // past the end of a row copies the row's first chunk instead; the
+    // fragment lanes holding it are zeroed after the read.
+    auto copy_k = [&](int t) {
+        t = t < nk ? t : nk - 1;
+        const int k0 = t * kBigK;
+        return (!ragged || k0 + goff < d) ? k0 : -goff;
+    };
+    auto copy_one = [&](int m, int kk, char* st) {
+        __builtin_amdgcn_global_load_lds(
+            (void*)(src[m] + kk), (__attribute__((address_space(3))) void*)(st + dst[m]), 16, 0, 0);
+    };
+    auto copy = [&](int t, char* st) {
+        const int kk = copy_k(t);
 #pragma unroll
-    for (int b = 0; b < kFR; ++b) {
-        const int rl = wr * kWaveR + b * kLmTile + r16;     // row within the block
+        for (int m = 0; m < NIW; ++m) copy_one(m, kk, st);
+    };
+
+    f32x4 acc[FV][FR];
+#pragma unroll
+    for (int a = 0; a < FV; ++a)
+#pragma unroll
+        for (int b = 0; b < FR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Fragment reads: lane (r16, kg) reads 16 bytes of row r16 of each
+    // fragment at k-chunk kg; every fragment's rows start at a multiple of
+    // 16, so the row's swizzle is (r16 >> 1) & 3 for all of them.
+    const int sw = (kg ^ ((r16 >> 1) & 3)) * 16;
+    const int aoff = (wv * FV * kLmTile + r16) * kBigRowBytes + sw;
+    const int boff = (TV + wr * FR * kLmTile + r16) * kBigRowBytes + sw;
+    u32x4 fa[FV], fb[FR];
+    auto read_frags = [&](const char* st) {
+#pragma unroll
+        for (int a = 0; a < FV; ++a)
+            fa[a] = *reinterpret_cast<const u32x4*>(st + aoff + a * kLmTile * kBigRowBytes);
+#pragma unroll
+        for (int b = 0; b < FR; ++b)
+            fb[b] = *reinterpret_cast<const u32x4*>(st + boff + b * kLmTile * kBigRowBytes);
+    };
+    // The reads have returned; k-chunk kg of step t past the end of the rows
+    // (last step, d not a multiple of 32) must contribute 0.
+    auto finish_frags = [&](int t) {
+        wait_lgkmcnt0();
+        if (ragged && t == nk - 1 && t * kBigK + kg * 8 >= d) {
+#pragma unroll
+            for (int a = 0; a < FV; ++a) fa[a] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int b = 0; b < FR; ++b) fb[b] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // The step's MFMAs, fragment row by fragment row, with this wave's copies
+    // of step t (into stage st) issued one after each of the first NIW rows:
+    // a copy that has to wait for the memory pipeline then stalls this wave
+    // while its MFMAs already issued keep the matrix unit busy.
+    static_assert(NIW <= FV, "one copy per fragment row at most");
+    auto mfmas_copy = [&](int t, char* st) {
+        const int kk = copy_k(t);
+#pragma unroll
+        for (int a = 0; a < FV; ++a) {
+#pragma unroll
+            for (int b = 0; b < FR; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, fa[a]), __builtin_bit_cast(bf16x8, fb[b]),
+                    acc[a][b], 0, 0, 0);
+            if (a < NIW) copy_one(a, kk, st);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Each group issues its copies of step t+S-1 during its own MFMAs of
+    // step t, into stage (t-1) % S, which both groups finished reading before
+    // Y_{t-1} (A, in Q_{t-2}) and X_{t-1} (B, in P_{t-1}).  Before X_t each
+    // wave needs its copies of step t+1 complete: group A issued them in
+    // P_{t-2} and has those of t+2 and t+3 (P_{t-1}, P_t) after them; group B
+    // in Q_{t-2}, with only those of t+2 (Q_{t-1}) after them.
+    if (!group_b) {
+        // Group A.  Prologue: copies of steps 0 .. S-2; step 0 whole; its fragments.
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t) copy(t, stage(t));
+        wait_vmcnt<(S - 2) * NIW>();
+        __builtin_amdgcn_s_barrier();
+        read_frags(st0);
+        finish_frags(0);
+        for (int t0 = 0; t0 < nk; t0 += S) {
+#pragma unroll
+            for (int h = 0; h < S; ++h) {
+                const int t = t0 + h;
+                if (t >= nk) break;
+                mfmas_copy(t + S - 1, stage((h + S - 1) % S));    // P_t
+                wait_vmcnt<(S - 2) * NIW>();
+                __builtin_amdgcn_s_barrier();                      // X_t
+                __builtin_amdgcn_sched_barrier(0);
+                read_frags(stage((h + 1) % S));                    // Q_t
+                finish_frags(t + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();                      // Y_t
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        // Group B.  Prologue: copies of steps 0 .. S-2; step 0 whole.
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t) copy(t, stage(t));
+        wait_vmcnt<(S - 2) * NIW>();
+        __builtin_amdgcn_s_barrier();
+        for (int t0 = 0; t0 < nk; t0 += S) {
+#pragma unroll
+            for (int h = 0; h < S; ++h) {
+                const int t = t0 + h;
+                if (t >= nk) break;
+                read_frags(stage(h));                              // P_t
+                finish_frags(t);
+                wait_vmcnt<(S - 3) * NIW>();
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();                      // X_t
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas_copy(t + S - 1, stage((h + S - 1) % S));    // Q_t
+                __builtin_amdgcn_s_barrier();                      // Y_t
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    wait_vmcnt<0>();                          // the trailing repeat copies
+
+    // Epilogue: lane holds D[vocab 4*kg + i][row r16] of each fragment, ids
+    // rising with (a, i).  Per fragment row b the lane stores its 32 logits
+    // (16-byte stores, the two fragments of a 128-byte line back to back),
+    // takes their maximum by a tree, the row's maximum over the four k-groups
+    // (lanes 16 apart), the first id holding it (independent compares against
+    // compile-time offsets; the lowest id of the row's four lanes), and the
+    // sum of exp(x - max) by the hardware exp2 into four independent sums.
+    // NaN never wins the maximum (fmaxf) nor the argmax (NaN == max is
+    // false); a row block past V masks its missing ids to -inf and keeps them
+    // out of the argmax.
+    const bool vec_store = (V & 3) == 0;
+    const bool inside = v0 + TV <= V;
+    constexpr int kNoId = 0x7fffffff;
+#pragma unroll
+    for (int b = 0; b < FR; ++b) {
+        const int rl = wr * FR * kLmTile + b * kLmTile + r16;     // row within the block
         const int r = r0 + rl;
         const bool row_ok = r < R;
+        const int vl = v0 + wv * FV * kLmTile + kg * 4;             // id of this lane's (a = 0, i = 0)
         float* lrow = logits ? logits + (size_t)(row_ok ? r : 0) * V : nullptr;
-        float mx = -INFINITY, av = -INFINITY;
-        int ai = -1;
+        if (row_ok && lrow) {
 #pragma unroll
-        for (int a = 0; a < kFV; ++a) {
-            const int v = v0 + wv * kWaveV + a * kLmTile + kg * 4;
-            if (row_ok && lrow) {
+            for (int a = 0; a < FV; ++a) {
+                const int v = vl + a * kLmTile;
                 if (vec_store) {
-                    if (v < V) *reinterpret_cast<float4*>(lrow + v) =
-                        make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+                    if (inside || v < V) *reinterpret_cast<f32x4*>(lrow + v) = acc[a][b];
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (v + i < V) lrow[v + i] = acc[a][b][i];
                 }
             }
+        }
+        float x[FV * 4];
+#pragma unroll
+        for (int a = 0; a < FV; ++a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (v + i < V) {
-                    mx = fmaxf(mx, acc[a][b][i]);
-                    if (acc[a][b][i] > av) { av = acc[a][b][i]; ai = v + i; }
-                }
-        }
+                x[a * 4 + i] = (inside || vl + a * kLmTile + i < V) ? acc[a][b][i] : -INFINITY;
+        float mt[FV * 2];
+#pragma unroll
+        for (int e = 0; e < FV * 2; ++e) mt[e] = fmaxf(x[2 * e], x[2 * e + 1]);
+#pragma unroll
+        for (int w = FV; w >= 1; w >>= 1)
+#pragma unroll
+            for (int e = 0; e < w; ++e) mt[e] = fmaxf(mt[e], mt[e + w]);
+        float mx = mt[0];
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // first id of the maximum, as an offset a * 16 + i from vl, scanned from the back
+        int off = kNoId;
 #pragma unroll
-        for (int off = 16; off < kWave; off <<= 1) {
-            const float av2 = __shfl_xor(av, off);
-            const int ai2 = __shfl_xor(ai, off);
-            arg_merge(av, ai, av2, ai2);
-        }
-        float sm = 0.f;
+        for (int e = FV * 4 - 1; e >= 0; --e)
+            off = (x[e] == mx && (inside || vl + (e >> 2) * kLmTile + (e & 3) < V))
+                      ? (e >> 2) * kLmTile + (e & 3) : off;
+        int ai = (mx == -INFINITY || off == kNoId) ? kNoId : vl + off;
+        ai = min(ai, __shfl_xor(ai, 16));
+        ai = min(ai, __shfl_xor(ai, 32));
+        float sm4[4] = {0.f, 0.f, 0.f, 0.f};
         if (mx != -INFINITY) {
 #pragma unroll
-            for (int a = 0; a < kFV; ++a) {
-                const int v = v0 + wv * kWaveV + a * kLmTile + kg * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (v + i < V) sm += expf(acc[a][b][i] - mx);
-            }
+            for (int e = 0; e < FV * 4; ++e) sm4[e & 3] += exp2_scaled(x[e] - mx);
         }
+        float sm = (sm4[0] + sm4[1]) + (sm4[2] + sm4[3]);
         sm += __shfl_xor(sm, 16);
         sm += __shfl_xor(sm, 32);
-        if (kg == 0) { s_max[wv][rl] = mx; s_sum[wv][rl] = sm; s_av[wv][rl] = av; s_ai[wv][rl] = ai; }
+        if (kg == 0) {
+            s_max[wv][rl] = mx;
+            s_sum[wv][rl] = sm;
+            s_av[wv][rl] = mx;
+            s_ai[wv][rl] = ai == kNoId ? -1 : ai;
+        }
     }
     __syncthreads();
-    if (threadIdx.x < TR && r0 + (int)threadIdx.x < R) {
-        const int rl = threadIdx.x;
+    for (int rl = threadIdx.x; rl < TR; rl += kBigNT) {
+        if (r0 + rl >= R) break;
         float m = -INFINITY, s = 0.f, av = -INFINITY;
         int ai = -1;
 #pragma unroll
@@ -256,18 +390,15 @@ __global__ __launch_bounds__(kBigThreads) void lmhead_big_kernel(
         part_sum[(size_t)(r0 + rl) * NPs + vb] = s;
         part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
     }
+    // The per-sequence counters of the stage-2 kernels start at zero (after
+    // the main loop, so these stores never sit in the copies' vmcnt queue).
+    for (int i = logical * kBigNT + threadIdx.x; i < n_counters; i += nblocks * kBigNT)
+        counters[i] = 0;
 }
 
 
 // ---------------------------------------------------------------------------
 // 64 < R <= 128: 256 x 128 blocks, W straight into registers, hidden rows in LDS.
-// s_waitcnt vmcnt(N), the other counters untouched (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // The pipelined path keeps four hidden-tile stages in LDS.
 constexpr int kStages = 4;
@@ -598,6 +729,21 @@ __global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
 }
 
 
+template <int FR>
+hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
+                      float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+                      int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
+    using C = BigCfg<FR>;
+    const int nvb = (V + C::TV - 1) / C::TV;
+    const int nrb = (R + C::TR - 1) / C::TR;
+    const int nblocks = nvb * nrb;
+    const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
+    lmhead_big_kernel<FR, 4><<<dim3(grid), dim3(kBigNT), 0, stream>>>(
+        hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
+        n_counters);
+    return hipGetLastError();
+}
+
 template <int FV, int FR, int WV, int WR, int U>
 hipError_t launch_shape(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
                         float* logits, float* part_max, float* part_sum, int32_t* part_arg,
@@ -632,27 +778,22 @@ hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R,
     if (R <= 128)
         return launch_shape<4, 8, 4, 1, 8>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
                                            NPs, counters, n_counters, stream);
-    // The row-block height that pads R least (ties to the taller block, whose
-    // W tile then serves more rows): R = 320 runs two blocks of 192 rows
-    // rather than two of 256, R = 1280 five of 256.
-    const int nvb = lmhead_tiled_partials(V);
-    int TR = 256;
-    for (int tr : {192, 128})
-        if ((R + tr - 1) / tr * tr < (R + TR - 1) / TR * TR) TR = tr;
-    const int nrb = (R + TR - 1) / TR;
-    const int nblocks = nvb * nrb;
-    const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
-    const dim3 g(grid), b(kBigThreads);
-    if (TR == 256)
-        lmhead_big_kernel<256, 2, 8, 4><<<g, b, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
-    else if (TR == 192)
-        lmhead_big_kernel<192, 4, 4, 6><<<g, b, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
-    else
-        lmhead_big_kernel<128, 4, 4, 4><<<g, b, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
-    return hipGetLastError();
+    // The row-block height (64 FR rows) that pads R least, ties to the taller
+    // block, whose W tile then serves more rows: R = 320 runs one block of
+    // 320 rows, R = 1280 four.
+    int FR = 5;
+    for (int fr : {4, 3, 2})
+        if ((R + 64 * fr - 1) / (64 * fr) * (64 * fr) < (R + 64 * FR - 1) / (64 * FR) * (64 * FR)) FR = fr;
+    switch (FR) {
+        case 5: return launch_big<5>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
+                                     counters, n_counters, stream);
+        case 4: return launch_big<4>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
+                                     counters, n_counters, stream);
+        case 3: return launch_big<3>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
+                                     counters, n_counters, stream);
+        default: return launch_big<2>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
+                                      counters, n_counters, stream);
+    }
 }
 
 }  // namespace sv

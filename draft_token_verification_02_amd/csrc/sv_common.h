@@ -126,6 +126,11 @@ struct TreeTopo {
     int8_t qslot[SV_MAX_TREE_NODES + 1];         // per row: its q row, -1 without children
 };
 
+// exp(x) for x <= 0 (or -inf) through the hardware exp2.
+__device__ __forceinline__ float exp2_scaled(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
 // Merge of two (max, sum of exp(x - max)) pairs: the online-softmax step.
 // Symmetric in its two arguments, so a butterfly gives every lane the same bits.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
