@@ -10,8 +10,11 @@ draw.  The timed loops call the library's two stage entry points back to back
 throughput; a second loop with HIP events around each LM-head launch gives
 that kernel's average duration for the roofline.  Prints one JSON line.
 
-Default workload: the Gemma-4-E2B-shaped head (d=1536, V=262144, gamma=4,
-B=1).  Other named workloads are in synth.inputs.CONFIGS.
+Default workload: the batch sweep's largest single-GPU case, sweep_b256_s0.5
+(d=4096, V=128256, gamma=4, B=256: 1280 rows, MFMA-bound), with the
+Gemma-4-E2B-shaped head at B=1 (d=1536, V=262144: HBM-bound) measured the
+same way as an extra entry.  Other named workloads are in
+synth.inputs.CONFIGS.
 
 Other modes (same JSON line):
   --mode greedy  greedy (match) verification: spec_verify_greedy, whose LM-head
@@ -115,59 +118,64 @@ def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
     return 2 * n / best / 1e9
 
 
-def cpu_baseline(x: dict, budget_s: float = 20.0, greedy: bool = False) -> dict:
-    """Time the fp64 oracle (as it stands) on the same inputs, on the host."""
-    from threadpoolctl import threadpool_info
+def _oracle_rate(x: dict, seqs: int, greedy: bool, budget_s: float, threads):
+    """Rows per second of the fp64 oracle (as it stands) on the first ``seqs``
+    sequences of the workload, with BLAS limited to ``threads`` (None: all);
+    median of up to three runs within ``budget_s``."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import greedy_ref, verify_ref
+    sub = {k: (v if k == "W_bits" else v[:seqs]) for k, v in x.items()}
     times = []
-    t_end = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
-        if greedy:
-            greedy_ref.verify_greedy(x["hidden_bits"], x["W_bits"], x["draft"])
-        else:
-            verify_ref.verify(x["hidden_bits"], x["W_bits"], x["draft"], x["q"], x["uniforms"])
-        times.append(time.perf_counter() - t0)
-        if len(times) >= 3 or time.perf_counter() + times[-1] > t_end:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    B, g1 = x["hidden_bits"].shape[:2]
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t_end = time.perf_counter() + budget_s
+        while True:
+            t0 = time.perf_counter()
+            if greedy:
+                greedy_ref.verify_greedy(sub["hidden_bits"], sub["W_bits"], sub["draft"])
+            else:
+                verify_ref.verify(sub["hidden_bits"], sub["W_bits"], sub["draft"], sub["q"],
+                                  sub["uniforms"])
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 3 or time.perf_counter() + times[-1] > t_end:
+                break
+    rows = seqs * x["hidden_bits"].shape[1]
     t = statistics.median(times)
-    return {"value": B * g1 / t, "unit": "positions/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(times)} full steps of the same workload (median {t:.2f} s per step, "
-                      f"fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()})"}
+    return rows / t, used, len(times), t
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="gemma_e2b")
-    ap.add_argument("--mode", choices=("sample", "greedy", "sparse", "tree", "head"),
-                    default="sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain device copy of this size (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the verification step here runs on a single MI355X)", file=sys.stderr)
-        sys.exit(2)
+def cpu_baseline(x: dict, greedy: bool = False, gpu_value: float = None) -> dict:
+    """The fp64 oracle (as it stands) timed on the host, on bounded samples of
+    the same workload: the first sequences of the batch, all host cores
+    (BLAS threads as the environment sets them), then one core.  The oracle
+    works sequence by sequence over full rows, so rows per second is its
+    positions/s on the whole batch."""
+    B, g1, d = x["hidden_bits"].shape
+    V = x["W_bits"].shape[0]
+    # samples sized for ~10 s of fp64 GEMM on a 16-core host / one core
+    per_seq = 2.0 * g1 * d * V
+    s_all = max(1, min(B, int(3.0e11 / per_seq)))
+    s_one = max(1, min(B, int(2.0e10 / per_seq)))
+    v_all, c_all, n_all, t_all = _oracle_rate(x, s_all, greedy, 30.0, None)
+    v_one, c_one, n_one, t_one = _oracle_rate(x, s_one, greedy, 30.0, 1)
+    res = {"value": v_all, "unit": "positions/s", "cores": c_all, "kind": "oracle",
+           "sample": f"first {s_all} of {B} sequences ({s_all * g1} rows x V={V}, d={d}), "
+                     f"median of {n_all} runs, {t_all:.2f} s each; fp64 numpy, "
+                     f"BLAS threads={c_all}, host cpus={os.cpu_count()}",
+           "single_core": {"value": v_one, "unit": "positions/s", "cores": c_one,
+                           "sample": f"first {s_one} sequences ({s_one * g1} rows), median of "
+                                     f"{n_one} runs, {t_one:.2f} s each"}}
+    if gpu_value:
+        res["gpu_over_oracle"] = gpu_value / v_all
+        res["gpu_over_oracle_single_core"] = gpu_value / v_one
+    return res
 
+
+def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
+    """Time ``steps`` whole steps of workload ``cfg`` in ``mode`` after
+    ``warmup`` untimed ones; returns (result dict, the host inputs)."""
     import numpy as np
     import torch
-
-    dev = torch.device("cuda:0")
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
-        return
 
     import draft_token_verification_02_amd as sv
     from synth import inputs
@@ -181,8 +189,6 @@ def main():
                 torch.from_numpy(np.ascontiguousarray(v)).pin_memory().to(dev)
                 for k, v in x.items()}
 
-    cfg = inputs.CONFIGS[args.config]
-    mode = args.mode
     stream = torch.cuda.current_stream(dev)
     extra_cfg = {}
     if mode == "tree":
@@ -272,12 +278,12 @@ def main():
         elif mode == "tree":
             whole()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         whole()
     torch.cuda.synchronize()
 
     # Timed region 1: K whole steps back to back -> value.
-    K = args.steps
+    K = steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
@@ -328,7 +334,7 @@ def main():
             step_bytes = perfmodel.step_bytes(B, g, d, V, int((n_host < g).sum()))
         # R <= 64 rows: the streaming kernel, one launch per 64 rows; more
         # rows: one launch of the pipelined 128-row GEMM (R <= 128) or of the
-        # LDS-tiled GEMM of 256-entry x 128/192/256-row blocks (when their
+        # ping-pong GEMM of 256-entry x 128-320-row blocks (when their
         # partials fit, as in every named workload).
         tiled = R > 64 and -(-V // 256) <= 1024
         passes = 1 if tiled else -(-R // 64)
@@ -350,14 +356,14 @@ def main():
     roof["alg_bytes_per_launch"] = lm_bytes // passes
     roof["hbm_GBps_alg"] = lm_bytes / lm_avg_s / 1e9
 
-    metric = ("verified positions/sec (fused LM-head + verify); LM-head HBM GB/s in roofline"
+    metric = ("verified positions/sec + achieved HBM GB/s (% roofline), fused LM-head+verify"
               if mode != "head" else "drafter head rows/sec (clustered sparse LM head)")
     res = {
         "metric": metric,
         "mode": mode,
         "value": R * K / elapsed,
         "unit": "positions/s" if mode != "head" else "rows/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "n_gpus": 1, "steps": K, "warmup": warmup,
         "ms_per_step": ms_per_step,
         "ms_per_step_with_lmhead_events": elapsed_ev * 1e3 / K,
         "higher_is_better": True,
@@ -383,12 +389,61 @@ def main():
         "mfma_busy_frac_counters": mfma_busy_from_counters(cfg.name) if mode == "sample" else None,
         "roofline": roof,
     }
-    res["achievable_copy_GBps"] = copy_bandwidth(dev)
     if n_host is not None:
         res["emitted_tokens_per_s"] = float((n_host + 1).sum()) * K / elapsed
         res["n_accepted"] = n_host.tolist()[:16]
-    if not args.no_cpu_baseline and mode in ("sample", "greedy"):
-        res["cpu_baseline"] = cpu_baseline(x, greedy=mode == "greedy")
+    del t, ws
+    torch.cuda.synchronize()
+    return res, x
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default="sweep_b256_s0.5")
+    ap.add_argument("--extra-config", default="gemma_e2b",
+                    help="a second workload measured the same way, reported under 'extra' "
+                         "('none' to skip)")
+    ap.add_argument("--mode", choices=("sample", "greedy", "sparse", "tree", "head"),
+                    default="sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the verification step here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
+
+    from synth import inputs
+
+    res, x = measure(inputs.CONFIGS[args.config], args.mode, args.steps, args.warmup, dev)
+    if args.extra_config != "none" and args.extra_config != args.config:
+        ex, _ = measure(inputs.CONFIGS[args.extra_config], args.mode, args.steps, args.warmup,
+                        dev)
+        keep = ("value", "unit", "ms_per_step", "steps_per_s", "step_GBps",
+                "step_frac_hbm_peak", "lmhead_ms_avg", "mfma_frac", "roofline", "config",
+                "emitted_tokens_per_s")
+        res["extra"] = {args.extra_config: {k: ex[k] for k in keep if k in ex}}
+    res["achievable_copy_GBps"] = copy_bandwidth(dev)
+    if not args.no_cpu_baseline and args.mode in ("sample", "greedy"):
+        res["cpu_baseline"] = cpu_baseline(x, greedy=args.mode == "greedy",
+                                           gpu_value=res["value"])
     print(json.dumps(res), flush=True)
 
 

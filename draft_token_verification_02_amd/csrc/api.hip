@@ -387,7 +387,8 @@ sv_status spec_verify_tree(const uint16_t* hidden, const uint16_t* W_lmhead, con
 
 sv_status sv_debug_views(const void* workspace, sv_dims dims, const float** logits,
                          const float** row_max, const float** row_sumexp, const int32_t** status) {
-    if (!dims_ok(dims)) return SV_ERR_DIMS;
+    // the dims of a chain call, or of a tree call (gamma = T, up to SV_MAX_TREE_NODES)
+    if (!dims_ok(dims) && !tree_dims_ok(dims)) return SV_ERR_DIMS;
     if (!workspace) return SV_ERR_NULL;
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     const char* base = static_cast<const char*>(workspace);

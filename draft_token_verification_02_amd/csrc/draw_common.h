@@ -505,6 +505,7 @@ __device__ int pick(DrawRow d, int b, int NC, const ChunkSums& cs, float u, unsi
 #pragma unroll
             for (int k = 0; k < kDrawWaves; ++k) s_wv[k] = wv[k];
         }
+        __builtin_amdgcn_wave_barrier();
         if (lane < kDrawWaves) wt = s_wv[lane];
     } else {
         double S = chunk_total_sum(tot, NC);

@@ -199,6 +199,8 @@ __global__ __launch_bounds__(kDrawBlock) void tree_init_kernel(
     if (threadIdx.x >= kWave) return;
     __shared__ NodeVal s_node[SV_MAX_TREE_NODES];
     node_table(node_keys(tp, b, a, r_m, r_s), tp, b, a, s_node);
+    // lane 0 reads the entries the other lanes of its wave just wrote
+    __builtin_amdgcn_wave_barrier();
     if (threadIdx.x == 0) {
         TreeState st;
         st.c = 0.0;
@@ -248,6 +250,7 @@ __device__ void tree_decide(TreeState st, const TreeTopo& tp, int b, const TreeA
     if (!draw && !(S > 0.0 && S < INFINITY)) draw = true;   // no residual mass: the pick falls back to p
     if (!draw) {
         node_table(keys, tp, b, a, s_node);
+        __builtin_amdgcn_wave_barrier();       // lane 0 reads the other lanes' entries
         if (lane == 0) {
             tree_advance(st, S, tp, b, a, s_node);
             state[b] = st;

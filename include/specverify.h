@@ -264,7 +264,9 @@ SV_API sv_status sv_sparse_head(const uint16_t *h, const uint16_t *W_lmhead,
                          int32_t *q_ids, float *q_vals, int32_t *clusters, void *workspace,
                          size_t workspace_bytes, void *hip_stream);
 
-/* Device pointers into `workspace` for inspection after a call completes:
+/* Device pointers into `workspace` for inspection after a call completes,
+ * for the dims that call was given (for spec_verify_tree: gamma = T, so R =
+ * B*(T+1) rows):
  *   logits      fp32 [R][V]
  *   row_max     fp32 [R]      max_v logits[r][v]
  *   row_sumexp  fp32 [R]      sum_v exp(logits[r][v] - row_max[r])

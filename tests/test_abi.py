@@ -85,7 +85,22 @@ def test_invalid_dims(dims):
     assert lib.spec_verify_sparse_q(p, p, p, p, p, 16, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     assert lib.sv_accept_and_draw_sparse_q(p, p, p, 16, p, d, p, p, p, 1 << 40, None) == _lib.SV_ERR_DIMS
     out = ctypes.c_void_p()
-    assert lib.sv_debug_views(p, d, ctypes.byref(out), None, None, None) == _lib.SV_ERR_DIMS
+    # the views also serve tree calls, whose gamma (T) may reach SV_MAX_TREE_NODES
+    want = _lib.SV_ERR_DIMS if _lib.tree_workspace_bytes(d) == 0 else _lib.SV_OK
+    assert lib.sv_debug_views(p, d, ctypes.byref(out), None, None, None) == want
+
+
+@no_device
+def test_debug_views_accept_tree_dims():
+    lib = _lib.library()
+    for T in (33, 64):
+        dims = _lib.Dims(6, T, 48, 600)
+        out = ctypes.c_void_p()
+        assert lib.sv_debug_views(ctypes.c_void_p(FAKE), dims, ctypes.byref(out), None, None,
+                                  None) == _lib.SV_OK
+        assert out.value == FAKE
+    assert lib.sv_debug_views(ctypes.c_void_p(FAKE), _lib.Dims(6, 65, 48, 600), None, None, None,
+                              None) == _lib.SV_ERR_DIMS
 
 
 @no_device

@@ -49,6 +49,9 @@ SMALL = [  # (B, parent, d, V, sigma, seed)
     (2, [-1] * 12, 48, 300, 2.0, 6),                # one wide fork
     (4, list(range(-1, 19)) + [0, 1], 64, 777, 0.5, 7),   # deep, two side branches
     (1, [-1, -1, 0, 0], 32, 280000, 1.0, 8),       # 69 chunks: split rounds, multi-window S
+    # the largest tree: 64 nodes, a 32-wide fork at the root and a 32-deep
+    # chain under its first child (one lane per node in the kernels' tables)
+    (6, [-1] * 32 + [0] + list(range(32, 63)), 48, 600, 0.7, 9),
 ]
 
 
