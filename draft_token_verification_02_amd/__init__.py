@@ -7,9 +7,11 @@ ABI, include/specverify.h); this package is its ctypes binding.
 from ._lib import (Dims, HeadDims, SVError, accept_and_draw, accept_and_draw_sparse_q,
                    accept_greedy, debug_views, dims_of, library, lmhead, new_workspace,
                    sparse_head, sparse_head_workspace_bytes, tree_shape, tree_workspace_bytes,
-                   verify, verify_greedy, verify_sparse_q, verify_tree, workspace_bytes)
+                   verify, verify_greedy, verify_sparse_q, verify_static, verify_tree,
+                   workspace_bytes)
 
 __all__ = ["Dims", "HeadDims", "SVError", "accept_and_draw", "accept_and_draw_sparse_q",
            "accept_greedy", "debug_views", "dims_of", "library", "lmhead", "new_workspace",
            "sparse_head", "sparse_head_workspace_bytes", "tree_shape", "tree_workspace_bytes",
-           "verify", "verify_greedy", "verify_sparse_q", "verify_tree", "workspace_bytes"]
+           "verify", "verify_greedy", "verify_sparse_q", "verify_static", "verify_tree",
+           "workspace_bytes"]

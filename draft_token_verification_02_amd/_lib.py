@@ -17,11 +17,13 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_DIMS, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_DEVICE = range(6)
 SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE, SV_DEV_BAD_QID = 1, 2, 4, 8
-ABI_VERSION = 3
+ABI_VERSION = 4
+STATIC_SCRATCH_BYTES = 48 << 20
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
            "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views",
            "spec_verify_sparse_q", "sv_accept_and_draw_sparse_q", "sv_sparse_head_workspace_bytes",
-           "sv_sparse_head", "sv_tree_shape", "sv_tree_workspace_bytes", "spec_verify_tree")
+           "sv_sparse_head", "sv_tree_shape", "sv_tree_workspace_bytes", "spec_verify_tree",
+           "spec_verify_static")
 
 
 class Dims(ctypes.Structure):
@@ -58,6 +60,8 @@ def _load():
         lib.sv_workspace_bytes.argtypes = [Dims]
         lib.spec_verify.restype = st
         lib.spec_verify.argtypes = [vp, vp, vp, vp, vp, Dims, vp, vp, vp, sz, vp]
+        lib.spec_verify_static.restype = st
+        lib.spec_verify_static.argtypes = [vp, vp, vp, vp, vp, Dims, vp, vp, vp]
         lib.sv_lmhead.restype = st
         lib.sv_lmhead.argtypes = [vp, vp, Dims, vp, sz, vp]
         lib.sv_accept_and_draw.restype = st
@@ -174,6 +178,31 @@ def verify(hidden, W, draft, q, uniforms, *, out_tokens=None, n_accepted=None, w
                              workspace.numel(), _stream_handle(dev, stream))
     if st != SV_OK:
         raise SVError(st, "spec_verify")
+    return out_tokens, n_accepted
+
+
+def verify_static(hidden, W, draft, q, uniforms, *, out_tokens=None, n_accepted=None,
+                  stream=None):
+    """spec_verify_static: the whole step with the library's static device
+    workspace (no workspace argument; the C call allocates nothing).  Pass
+    preallocated outputs to allocate nothing here either.  Calls on one device
+    share that workspace: serialise them."""
+    import torch
+    _check_inputs(hidden, W, draft, q, uniforms)
+    dims = dims_of(hidden, W)
+    dev = W.device
+    if out_tokens is None:
+        out_tokens = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((dims.B,), dtype=torch.int32, device=dev)
+    st = _load().spec_verify_static(_ptr(hidden), _ptr(W), _ptr(draft), _ptr(q), _ptr(uniforms),
+                                    dims, _ptr(out_tokens), _ptr(n_accepted),
+                                    _stream_handle(dev, stream))
+    if st == SV_ERR_WORKSPACE:
+        raise SVError(st, f"spec_verify_static: these dims need {workspace_bytes(dims)} bytes of "
+                          f"workspace, more than the static {STATIC_SCRATCH_BYTES}")
+    if st != SV_OK:
+        raise SVError(st, "spec_verify_static")
     return out_tokens, n_accepted
 
 

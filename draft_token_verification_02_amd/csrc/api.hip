@@ -3,6 +3,7 @@
 // caller's stream.  No allocation, no synchronisation, no state.
 
 #include <algorithm>
+#include <mutex>
 
 #include "sv_common.h"
 
@@ -206,6 +207,32 @@ sv_status check_greedy(const int32_t* draft, sv_dims dims, const int32_t* out_to
     return check_workspace(ws, bytes, dims);
 }
 
+// Workspace of spec_verify_static: a file-scope device array, which every
+// device the library runs on holds from module load until the process ends.
+// In host code its name only stands in for it; its address on a device comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address goes to the kernels.
+constexpr size_t kStaticScratchBytes = SV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+sv_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_DEVICE;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return SV_ERR_DEVICE;
+    *out = g_scratch_ptr[dev];
+    return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +284,24 @@ sv_status spec_verify(const uint16_t* hidden, const uint16_t* W_lmhead, const in
     st = stage1(hidden, W_lmhead, dims, workspace, s);
     if (st != SV_OK) return st;
     return stage2(draft_tokens, q, nullptr, 0, uniforms, dims, out_tokens, n_accepted, workspace, s);
+}
+
+sv_status spec_verify_static(const uint16_t* hidden, const uint16_t* W_lmhead,
+                             const int32_t* draft_tokens, const float* q, const float* uniforms,
+                             sv_dims dims, int32_t* out_tokens, int32_t* n_accepted,
+                             void* hip_stream) {
+    if (!dims_ok(dims)) return SV_ERR_DIMS;
+    if (!hidden || !W_lmhead || !draft_tokens || !q || !uniforms || !out_tokens || !n_accepted)
+        return SV_ERR_NULL;
+    if (sv_workspace_bytes(dims) > kStaticScratchBytes) return SV_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const sv_status got = scratch_on_current_device(&ws);
+    if (got != SV_OK) return got;
+    // The same launches as spec_verify; the LM-head kernel zeroes the
+    // per-sequence counters the draw kernels use, so nothing in the array
+    // needs clearing first.
+    return spec_verify(hidden, W_lmhead, draft_tokens, q, uniforms, dims, out_tokens, n_accepted,
+                       ws, kStaticScratchBytes, hip_stream);
 }
 
 sv_status sv_accept_and_draw_sparse_q(const int32_t* draft_tokens, const int32_t* q_ids,

@@ -56,7 +56,7 @@ extern "C" {
 #define SV_API
 #endif
 
-#define SV_ABI_VERSION 3
+#define SV_ABI_VERSION 4
 #define SV_MAX_GAMMA 32
 
 typedef struct {
@@ -106,6 +106,27 @@ SV_API sv_status spec_verify(const uint16_t *hidden, const uint16_t *W_lmhead,
                       const int32_t *draft_tokens, const float *q, const float *uniforms,
                       sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* spec_verify for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): no
+ * workspace argument; the workspace is a static device array of the library,
+ * SV_STATIC_SCRATCH_BYTES on every device it runs on, kept until the process
+ * ends.  Other arguments, results and conventions as for spec_verify.
+ *   - Returns SV_ERR_WORKSPACE, before anything is enqueued, when
+ *     sv_workspace_bytes(dims) exceeds SV_STATIC_SCRATCH_BYTES (48 MiB: up
+ *     to 45 rows at V = 262144, 95 rows at V = 128256).
+ *   - Allocates nothing.  The first call on a device looks the array's
+ *     address up on the current device (hipGetSymbolAddress); `hip_stream`
+ *     must belong to that device.  SV_ERR_DEVICE if the lookup fails.
+ *   - Every call on one device uses the same array, which keeps the last
+ *     call's contents (no clearing is needed: the step resets what it uses).
+ *     Calls that can overlap on one device (different streams or host
+ *     threads) race on it; the caller must serialise them. */
+#define SV_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+SV_API sv_status spec_verify_static(const uint16_t *hidden, const uint16_t *W_lmhead,
+                             const int32_t *draft_tokens, const float *q, const float *uniforms,
+                             sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,
+                             void *hip_stream);
 
 /* Stage 1 alone: the LM-head GEMM for all R rows in one pass over W, writing
  * the fp32 logits and per-tile softmax and argmax partials into the workspace.

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for name in _declared():
         assert hasattr(raw, name), name
-    assert lib.sv_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.sv_abi_version() == _lib.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -290,3 +290,22 @@ def test_tree_argument_errors_return_before_launch():
     assert lib.spec_verify_tree(p, p, pp, p, p, p, d, p, p, odd, p, n, None) == _lib.SV_ERR_ALIGN
     assert lib.spec_verify_tree(p, p, pp, p, p, p, d, p, p, None, p, n - 1, None) == \
         _lib.SV_ERR_WORKSPACE
+
+
+@no_device
+def test_static_entry_point_errors_return_before_any_device_call():
+    lib = _lib.library()
+    p = ctypes.c_void_p(FAKE)
+    ok = _lib.Dims(4, 4, 64, 1000)
+    big = _lib.Dims(20, 4, 64, 128256)                 # 100 rows x 128256: 52.7 MB
+    assert _lib.workspace_bytes(big) > _lib.STATIC_SCRATCH_BYTES
+    assert lib.spec_verify_static(p, p, p, p, p, big, p, p, None) == _lib.SV_ERR_WORKSPACE
+    assert lib.spec_verify_static(p, p, p, p, p, _lib.Dims(0, 4, 64, 1000), p, p, None) == \
+        _lib.SV_ERR_DIMS
+    for i in range(7):
+        args = [p] * 7
+        args[i] = None
+        assert lib.spec_verify_static(*args[:5], ok, *args[5:], None) == _lib.SV_ERR_NULL
+    # the largest row counts the 48 MiB array holds at the two head shapes
+    assert _lib.workspace_bytes(_lib.Dims(9, 4, 1536, 262144)) <= _lib.STATIC_SCRATCH_BYTES
+    assert _lib.workspace_bytes(_lib.Dims(19, 4, 4096, 128256)) <= _lib.STATIC_SCRATCH_BYTES
