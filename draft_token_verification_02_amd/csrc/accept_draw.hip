@@ -283,20 +283,14 @@ __global__ __launch_bounds__(kWave) void pick_kernel(
 // 7.7 us inline at B = 1 over 64 chunks, 8.4 vs 8.0 us at B = 4 over 32
 // chunks (and 10.8 us split), and 15.6 vs 9.6 us at 512 workgroups, where the
 // workgroups' device-scope releases cost more than the pick's extra launch.
-#ifndef SV_FUSE_MAX_GROUPS
-#define SV_FUSE_MAX_GROUPS 64
-#endif
+constexpr int kFuseMaxGroups = 64;
 // Sparse q has no inline form (below), so it stays fused up to 256.
-#ifndef SV_FUSE_MAX_GROUPS_SPARSE
-#define SV_FUSE_MAX_GROUPS_SPARSE 256
-#endif
+constexpr int kFuseMaxGroupsSparse = 256;
 // Inline form from 65 to 1024 draw workgroups: 11.2 -> 9.6 us at 512
 // (B = 8 over 64 chunks, B = 16 over 32); at 2048 it measured 24.2 us against
 // 20.8 us split, where every workgroup repeating the accept tests costs more
 // than the accept launch.
-#ifndef SV_INLINE_MAX_GROUPS
-#define SV_INLINE_MAX_GROUPS 1024
-#endif
+constexpr int kInlineMaxGroups = 1024;
 
 namespace {
 
@@ -313,7 +307,7 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
     // the pick (two launches; no device-scope arrival per workgroup).  Many:
     // accept once per sequence, chunk totals, then the pick -- three
     // launches, no workgroup repeats the accept tests.
-    if (groups <= (SPARSE ? SV_FUSE_MAX_GROUPS_SPARSE : SV_FUSE_MAX_GROUPS)) {
+    if (groups <= (SPARSE ? kFuseMaxGroupsSparse : kFuseMaxGroups)) {
         draw_kernel<kDrawFused, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
             logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
             row_max, row_sum, out_tokens, n_accepted, status);
@@ -322,7 +316,7 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
     hipError_t e;
     // (Sparse q stays split: repeating its id lookups in every workgroup
     // measured slower, 172.3 -> 175.7 us per step at B = 8.)
-    if (!SPARSE && groups <= SV_INLINE_MAX_GROUPS) {
+    if (!SPARSE && groups <= kInlineMaxGroups) {
         draw_kernel<kDrawInline, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
             logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
             row_max, row_sum, out_tokens, n_accepted, status);

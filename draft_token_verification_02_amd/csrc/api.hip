@@ -3,6 +3,7 @@
 // caller's stream.  No allocation, no synchronisation, no state.
 
 #include <algorithm>
+#include <cstring>
 #include <mutex>
 
 #include "sv_common.h"
@@ -240,7 +241,11 @@ extern "C" {
 int32_t sv_abi_version(void) { return SV_ABI_VERSION; }
 
 const char* sv_status_string(sv_status status) {
-    switch (status) {
+    // A C caller may pass any int: read the argument's bytes as one rather
+    // than loading an enum value outside the enum's range.
+    int code;
+    std::memcpy(&code, &status, sizeof code);
+    switch (code) {
         case SV_OK: return "SV_OK";
         case SV_ERR_NULL: return "SV_ERR_NULL: a required pointer is NULL";
         case SV_ERR_DIMS: return "SV_ERR_DIMS: a dimension is outside the supported limits";

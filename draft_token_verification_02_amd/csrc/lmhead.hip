@@ -33,20 +33,6 @@
 
 #include "sv_common.h"
 
-#ifndef SV_LM_WG_PER_CU
-#define SV_LM_WG_PER_CU 1
-#endif
-// Fragments of 16 vocab rows per wave the grid aims at; 0 = persistent (one
-// workgroup per CU, the vocabulary split over them).
-#ifndef SV_LM_TILES_PER_WAVE
-#define SV_LM_TILES_PER_WAVE 0
-#endif
-// Start each fragment group's walk over k at a hashed offset (see the
-// streaming loop); 0 walks every group from k = 0.
-#ifndef SV_LM_ROTATE
-#define SV_LM_ROTATE 1
-#endif
-
 namespace sv {
 
 namespace {
@@ -57,35 +43,11 @@ namespace {
 // fragment (one fragment loses once the 16 hidden rows are distinct: its
 // hidden loads match its W loads byte for byte); more fragments, to share
 // each hidden-row load, and shallower rings as MT grows.
-#ifndef SV_LM1_T
-#define SV_LM1_T 2
-#endif
-#ifndef SV_LM1_U
-#define SV_LM1_U 4
-#endif
-#ifndef SV_LM2_T
-#define SV_LM2_T 4
-#endif
-#ifndef SV_LM2_U
-#define SV_LM2_U 2
-#endif
-#ifndef SV_LM3_T
-#define SV_LM3_T 8
-#endif
-#ifndef SV_LM3_U
-#define SV_LM3_U 2
-#endif
-#ifndef SV_LM4_T
-#define SV_LM4_T 8
-#endif
-#ifndef SV_LM4_U
-#define SV_LM4_U 2
-#endif
 template <int MT> struct LmCfg;
-template <> struct LmCfg<1> { static constexpr int T = SV_LM1_T, U = SV_LM1_U; };
-template <> struct LmCfg<2> { static constexpr int T = SV_LM2_T, U = SV_LM2_U; };
-template <> struct LmCfg<3> { static constexpr int T = SV_LM3_T, U = SV_LM3_U; };
-template <> struct LmCfg<4> { static constexpr int T = SV_LM4_T, U = SV_LM4_U; };
+template <> struct LmCfg<1> { static constexpr int T = 2, U = 4; };
+template <> struct LmCfg<2> { static constexpr int T = 4, U = 2; };
+template <> struct LmCfg<3> { static constexpr int T = 8, U = 2; };
+template <> struct LmCfg<4> { static constexpr int T = 8, U = 2; };
 constexpr int kGenericU = 4;         // ring depth of the path for ragged d
 
 // Groups of T fragments a wave stages in LDS before writing them out: a
@@ -382,7 +344,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
             // with the offsets spread).
             const int nblk = nstep / U;
             auto rot = [&](int g) {
-                return SV_LM_ROTATE ? (int)(((unsigned)g * 2654435761u >> 16) % (unsigned)nblk) * U : 0;
+                return (int)(((unsigned)g * 2654435761u >> 16) % (unsigned)nblk) * U;
             };
             int lcnt = 0;                 // k-steps loaded in the current load group
             lk = rot(lg);
@@ -515,16 +477,12 @@ void launch_mt(dim3 g, dim3 b, hipStream_t s, const uint16_t* hidden, const uint
 // row): one per compute unit, capped so every wave has fragments to stream.
 int lmhead_grid(int V) {
     const int ntiles = (V + kLmTile - 1) / kLmTile;
-    if (SV_LM_TILES_PER_WAVE > 0) {
-        const int per_wg = SV_LM_TILES_PER_WAVE * kLmWaves;
-        return max(1, min((ntiles + per_wg - 1) / per_wg, lmhead_useful_groups(V)));
-    }
     // One workgroup per CU at most, and just enough of them that every wave
     // gets the same number of fragment groups (measured on the grouping of
     // the one-hidden-fragment configuration, which all row counts share).
     const int T1 = LmCfg<1>::T;
     const int ngroups = (ntiles + T1 - 1) / T1;
-    const int waves = cu_count() * SV_LM_WG_PER_CU * kLmWaves;
+    const int waves = cu_count() * kLmWaves;
     const int per_wave = (ngroups + waves - 1) / waves;
     const int grid = (ngroups + per_wave * kLmWaves - 1) / (per_wave * kLmWaves);
     return max(1, min(grid, lmhead_useful_groups(V)));

@@ -18,19 +18,13 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;              // threads per greedy and drafter-head workgroup
 
 constexpr int kLmTile = 16;              // vocab rows (and hidden rows) per MFMA fragment
-#ifndef SV_LM_WAVES
-#define SV_LM_WAVES 4
-#endif
-constexpr int kLmWaves = SV_LM_WAVES;    // waves per LM-head workgroup
+constexpr int kLmWaves = 4;              // waves per LM-head workgroup
 constexpr int kLmMaxPartials = 1024;     // LM-head workgroups (softmax partials per row), at most
 constexpr int kLmRowsPerPass = 64;       // hidden rows one LM-head launch handles
 // Draw and tree kernels: 1024 threads (four waves per SIMD, so that one
 // wave's dependent arithmetic hides behind the others') over 4096-token
 // chunks, four tokens per thread.
-#ifndef SV_DRAW_BLOCK
-#define SV_DRAW_BLOCK 1024
-#endif
-constexpr int kDrawBlock = SV_DRAW_BLOCK;
+constexpr int kDrawBlock = 1024;
 constexpr int kDrawChunk = 4096;                                                // tokens per chunk
 constexpr int kDrawPerThread = kDrawChunk / kDrawBlock;
 constexpr int kDrawWaves = kDrawBlock / kWave;

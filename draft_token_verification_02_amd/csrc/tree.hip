@@ -310,9 +310,9 @@ __global__ __launch_bounds__(kDrawBlock) void tree_round_kernel(
 
 }  // namespace
 
-#ifndef SV_TREE_FUSE_MAX_GROUPS
-#define SV_TREE_FUSE_MAX_GROUPS 64
-#endif
+// One fused launch per round up to 64 chunk workgroups (moving the threshold
+// to 256 or 1024 changed nothing measurable), two above.
+constexpr int kTreeFuseMaxGroups = 64;
 
 hipError_t launch_tree(const float* logits, const float* part_max, const float* part_sum, int NP,
                        int NPs, int B, int V, const TreeTopo& tp, int rounds,
@@ -331,7 +331,7 @@ hipError_t launch_tree(const float* logits, const float* part_max, const float* 
     const unsigned groups = (unsigned)B * NC;
     // Few chunk workgroups: one fused launch per round (see draw_kernel for
     // why many sequences use the split form instead).
-    const bool fused = groups <= SV_TREE_FUSE_MAX_GROUPS;
+    const bool fused = groups <= kTreeFuseMaxGroups;
     for (int r = 0; r < rounds && e == hipSuccess; ++r) {
         if (fused) {
             tree_round_kernel<<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
