@@ -8,7 +8,9 @@ normalisers, the accept tests, the first rejection and the replacement/bonus
 draw.  The timed loops call the library's two stage entry points back to back
 (exactly the launches spec_verify makes).  The first loop gives the
 throughput; a second loop with HIP events around each LM-head launch gives
-that kernel's average duration for the roofline.  Prints one JSON line.
+that kernel's average duration for the roofline.  (Stage 1 is launched as
+spec_verify launches it: sv_lmhead_ex keeping the logits, without the argmax
+partials only greedy verification reads.)  Prints one JSON line.
 
 Default workload: the batch sweep's largest single-GPU case, sweep_b256_s0.5
 (d=4096, V=128256, gamma=4, B=256: 1280 rows, MFMA-bound), with the
@@ -212,7 +214,7 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
                            workspace=ws, stream=stream)
 
         def lm_only():
-            sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream)
+            sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream, argmax=False)
     elif mode == "head":
         if cfg.sparse is None:
             raise SystemExit("--mode head needs a workload with clusters (e.g. --config sparse_q)")
@@ -254,7 +256,8 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
                 sv.verify_greedy(t["hidden_bits"], t["W_bits"], t["draft"], out_tokens=out,
                                  n_accepted=n_acc, target_tokens=tgt, workspace=ws, stream=stream)
             else:
-                sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream)
+                # what spec_verify launches: logits kept, no argmax partials
+                sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream, argmax=False)
 
         def stage2():
             if mode == "sample":

@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_DIMS, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_DEVICE = range(6)
 SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE, SV_DEV_BAD_QID = 1, 2, 4, 8
+SV_LMHEAD_LOGITS, SV_LMHEAD_ARGMAX = 1, 2
 ABI_VERSION = 4
 STATIC_SCRATCH_BYTES = 48 << 20
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
            "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views",
            "spec_verify_sparse_q", "sv_accept_and_draw_sparse_q", "sv_sparse_head_workspace_bytes",
            "sv_sparse_head", "sv_tree_shape", "sv_tree_workspace_bytes", "spec_verify_tree",
-           "spec_verify_static")
+           "spec_verify_static", "sv_lmhead_ex")
 
 
 class Dims(ctypes.Structure):
@@ -62,6 +63,8 @@ def _load():
         lib.spec_verify.argtypes = [vp, vp, vp, vp, vp, Dims, vp, vp, vp, sz, vp]
         lib.spec_verify_static.restype = st
         lib.spec_verify_static.argtypes = [vp, vp, vp, vp, vp, Dims, vp, vp, vp]
+        lib.sv_lmhead_ex.restype = st
+        lib.sv_lmhead_ex.argtypes = [vp, vp, Dims, ctypes.c_int32, vp, sz, vp]
         lib.sv_lmhead.restype = st
         lib.sv_lmhead.argtypes = [vp, vp, Dims, vp, sz, vp]
         lib.sv_accept_and_draw.restype = st
@@ -244,12 +247,19 @@ def accept_greedy(dims: Dims, draft, out_tokens, n_accepted, workspace, *, targe
         raise SVError(st, "sv_accept_greedy")
 
 
-def lmhead(hidden, W, workspace, *, stream=None):
-    """Stage 1: logits and softmax partials into ``workspace``."""
+def lmhead(hidden, W, workspace, *, stream=None, logits=True, argmax=True):
+    """Stage 1: softmax partials into ``workspace``, with the logits and the
+    argmax partials unless asked not to (sv_lmhead, or sv_lmhead_ex with the
+    matching flags: logits=True, argmax=False launches what spec_verify does)."""
     _check_inputs(hidden, W)
     dims = dims_of(hidden, W)
-    st = _load().sv_lmhead(_ptr(hidden), _ptr(W), dims, _ptr(workspace), workspace.numel(),
-                           _stream_handle(W.device, stream))
+    if logits and argmax:
+        st = _load().sv_lmhead(_ptr(hidden), _ptr(W), dims, _ptr(workspace), workspace.numel(),
+                               _stream_handle(W.device, stream))
+    else:
+        flags = (SV_LMHEAD_LOGITS if logits else 0) | (SV_LMHEAD_ARGMAX if argmax else 0)
+        st = _load().sv_lmhead_ex(_ptr(hidden), _ptr(W), dims, flags, _ptr(workspace),
+                                  workspace.numel(), _stream_handle(W.device, stream))
     if st != SV_OK:
         raise SVError(st, "sv_lmhead")
 

@@ -66,21 +66,24 @@ sv_status check_workspace(const void* ws, size_t bytes, sv_dims dims) {
     return SV_OK;
 }
 
-// keep_logits = false (greedy verification) writes only the partials.
+// keep_logits = false (greedy verification) writes only the partials;
+// with_argmax = false leaves out the greedy candidates (part_arg), which only
+// greedy verification reads.
 sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* ws, hipStream_t s,
-                 bool keep_logits = true) {
+                 bool keep_logits = true, bool with_argmax = true) {
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     float* logits = keep_logits ? at<float>(ws, L.logits) : nullptr;
+    int32_t* part_arg = with_argmax ? at<int32_t>(ws, L.part_arg) : nullptr;
     hipError_t e;
     if (sv::lmhead_use_tiled(L.R, dims.V))
         e = sv::launch_lmhead_tiled(hidden, W, L.R, dims.d, dims.V, logits,
                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
-                                    at<int32_t>(ws, L.part_arg), L.NPs,
+                                    part_arg, L.NPs,
                                     at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
     else
         e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, logits,
                               at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
-                              at<int32_t>(ws, L.part_arg), L.NPs, sv::lmhead_grid(dims.V),
+                              part_arg, L.NPs, sv::lmhead_grid(dims.V),
                               at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
@@ -268,6 +271,15 @@ sv_status sv_lmhead(const uint16_t* hidden, const uint16_t* W_lmhead, sv_dims di
     return stage1(hidden, W_lmhead, dims, workspace, static_cast<hipStream_t>(hip_stream));
 }
 
+sv_status sv_lmhead_ex(const uint16_t* hidden, const uint16_t* W_lmhead, sv_dims dims, int32_t flags,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (flags & ~(SV_LMHEAD_LOGITS | SV_LMHEAD_ARGMAX)) return SV_ERR_DIMS;
+    const sv_status st = check_stage1(hidden, W_lmhead, dims, workspace, workspace_bytes);
+    if (st != SV_OK) return st;
+    return stage1(hidden, W_lmhead, dims, workspace, static_cast<hipStream_t>(hip_stream),
+                  (flags & SV_LMHEAD_LOGITS) != 0, (flags & SV_LMHEAD_ARGMAX) != 0);
+}
+
 sv_status sv_accept_and_draw(const int32_t* draft_tokens, const float* q, const float* uniforms,
                              sv_dims dims, int32_t* out_tokens, int32_t* n_accepted, void* workspace,
                              size_t workspace_bytes, void* hip_stream) {
@@ -286,7 +298,7 @@ sv_status spec_verify(const uint16_t* hidden, const uint16_t* W_lmhead, const in
     st = check_stage2(draft_tokens, q, uniforms, dims, out_tokens, n_accepted, workspace, workspace_bytes);
     if (st != SV_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    st = stage1(hidden, W_lmhead, dims, workspace, s);
+    st = stage1(hidden, W_lmhead, dims, workspace, s, /*keep_logits=*/true, /*with_argmax=*/false);
     if (st != SV_OK) return st;
     return stage2(draft_tokens, q, nullptr, 0, uniforms, dims, out_tokens, n_accepted, workspace, s);
 }
@@ -331,7 +343,7 @@ sv_status spec_verify_sparse_q(const uint16_t* hidden, const uint16_t* W_lmhead,
                              n_accepted, workspace, workspace_bytes);
     if (st != SV_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    st = stage1(hidden, W_lmhead, dims, workspace, s);
+    st = stage1(hidden, W_lmhead, dims, workspace, s, /*keep_logits=*/true, /*with_argmax=*/false);
     if (st != SV_OK) return st;
     return stage2(draft_tokens, q_vals, q_ids, K, uniforms, dims, out_tokens, n_accepted,
                   workspace, s);
@@ -421,7 +433,8 @@ sv_status spec_verify_tree(const uint16_t* hidden, const uint16_t* W_lmhead, con
         return SV_ERR_ALIGN;
     if (workspace_bytes < sv_tree_workspace_bytes(dims)) return SV_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const sv_status st = stage1(hidden, W_lmhead, dims, workspace, s);
+    const sv_status st = stage1(hidden, W_lmhead, dims, workspace, s, /*keep_logits=*/true,
+                                /*with_argmax=*/false);
     if (st != SV_OK) return st;
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     const hipError_t e = sv::launch_tree(

@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         if ((threadIdx.x & 3) == 0) {
             part_max[(size_t)(row0 + prow) * NPs + blockIdx.x] = m;
             part_sum[(size_t)(row0 + prow) * NPs + blockIdx.x] = s;
-            part_arg[(size_t)(row0 + prow) * NPs + blockIdx.x] = ai;
+            if (part_arg) part_arg[(size_t)(row0 + prow) * NPs + blockIdx.x] = ai;
         }
     }
 }

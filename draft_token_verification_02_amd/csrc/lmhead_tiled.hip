@@ -117,7 +117,7 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-template <int FR, int S>
+template <int FR, int S, bool ARG>
 __global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
@@ -254,6 +254,11 @@ __global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
     // wave needs its copies of step t+1 complete: group A issued them in
     // P_{t-2} and has those of t+2 and t+3 (P_{t-1}, P_t) after them; group B
     // in Q_{t-2}, with only those of t+2 (Q_{t-1}) after them.
+    // Copies outstanding when a wave's copies of step t+1 are complete, at
+    // X_t: those issued during step t-1, and for group A (whose MFMA phase
+    // comes first) those of step t.
+    constexpr int kWaitA = (S - 2) * NIW;
+    constexpr int kWaitB = (S - 3) * NIW;
     if (!group_b) {
         // Group A.  Prologue: copies of steps 0 .. S-2; step 0 whole; its fragments.
 #pragma unroll
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
                 const int t = t0 + h;
                 if (t >= nk) break;
                 mfmas_copy(t + S - 1, stage((h + S - 1) % S));    // P_t
-                wait_vmcnt<(S - 2) * NIW>();
+                wait_vmcnt<kWaitA>();
                 __builtin_amdgcn_s_barrier();                      // X_t
                 __builtin_amdgcn_sched_barrier(0);
                 read_frags(stage((h + 1) % S));                    // Q_t
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
                 if (t >= nk) break;
                 read_frags(stage(h));                              // P_t
                 finish_frags(t);
-                wait_vmcnt<(S - 3) * NIW>();
+                wait_vmcnt<kWaitB>();
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();                      // X_t
                 __builtin_amdgcn_sched_barrier(0);
@@ -352,15 +357,19 @@ __global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
         float mx = mt[0];
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // first id of the maximum, as an offset a * 16 + i from vl, scanned from the back
-        int off = kNoId;
+        // first id of the maximum, as an offset a * 16 + i from vl, scanned
+        // from the back (greedy candidates; skipped when nobody reads them)
+        int ai = kNoId;
+        if constexpr (ARG) {
+            int off = kNoId;
 #pragma unroll
-        for (int e = FV * 4 - 1; e >= 0; --e)
-            off = (x[e] == mx && (inside || vl + (e >> 2) * kLmTile + (e & 3) < V))
-                      ? (e >> 2) * kLmTile + (e & 3) : off;
-        int ai = (mx == -INFINITY || off == kNoId) ? kNoId : vl + off;
-        ai = min(ai, __shfl_xor(ai, 16));
-        ai = min(ai, __shfl_xor(ai, 32));
+            for (int e = FV * 4 - 1; e >= 0; --e)
+                off = (x[e] == mx && (inside || vl + (e >> 2) * kLmTile + (e & 3) < V))
+                          ? (e >> 2) * kLmTile + (e & 3) : off;
+            ai = (mx == -INFINITY || off == kNoId) ? kNoId : vl + off;
+            ai = min(ai, __shfl_xor(ai, 16));
+            ai = min(ai, __shfl_xor(ai, 32));
+        }
         float sm4[4] = {0.f, 0.f, 0.f, 0.f};
         if (mx != -INFINITY) {
 #pragma unroll
@@ -384,11 +393,11 @@ __global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
 #pragma unroll
         for (int w = 0; w < WV; ++w) {
             lse_merge(m, s, s_max[w][rl], s_sum[w][rl]);
-            arg_merge(av, ai, s_av[w][rl], s_ai[w][rl]);
+            if (ARG) arg_merge(av, ai, s_av[w][rl], s_ai[w][rl]);
         }
         part_max[(size_t)(r0 + rl) * NPs + vb] = m;
         part_sum[(size_t)(r0 + rl) * NPs + vb] = s;
-        part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
+        if (ARG) part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
     }
     // The per-sequence counters of the stage-2 kernels start at zero (after
     // the main loop, so these stores never sit in the copies' vmcnt queue).
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(WV * WR * kWave) void lmhead_mid_kernel(
         }
         part_max[(size_t)(r0 + rl) * NPs + vb] = m;
         part_sum[(size_t)(r0 + rl) * NPs + vb] = s;
-        part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
+        if (part_arg) part_arg[(size_t)(r0 + rl) * NPs + vb] = ai;
     }
 }
 
@@ -738,9 +747,14 @@ hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, int R, int d, i
     const int nrb = (R + C::TR - 1) / C::TR;
     const int nblocks = nvb * nrb;
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
-    lmhead_big_kernel<FR, 4><<<dim3(grid), dim3(kBigNT), 0, stream>>>(
-        hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
-        n_counters);
+    if (part_arg)
+        lmhead_big_kernel<FR, 4, true><<<dim3(grid), dim3(kBigNT), 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
+            n_counters);
+    else
+        lmhead_big_kernel<FR, 4, false><<<dim3(grid), dim3(kBigNT), 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
+            n_counters);
     return hipGetLastError();
 }
 

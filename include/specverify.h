@@ -134,6 +134,19 @@ SV_API sv_status spec_verify_static(const uint16_t *hidden, const uint16_t *W_lm
 SV_API sv_status sv_lmhead(const uint16_t *hidden, const uint16_t *W_lmhead, sv_dims dims,
                     void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Stage 1 with a choice of what it stores: flags is a bitwise OR of
+ *   SV_LMHEAD_LOGITS  the fp32 logits, which sv_accept_and_draw, its sparse-q
+ *                     form and sv_debug_views read
+ *   SV_LMHEAD_ARGMAX  the argmax partials, which sv_accept_greedy reads
+ * (the softmax partials are always stored).  sv_lmhead is
+ * flags = SV_LMHEAD_LOGITS | SV_LMHEAD_ARGMAX; spec_verify, spec_verify_static,
+ * spec_verify_sparse_q and spec_verify_tree launch SV_LMHEAD_LOGITS; spec_verify_greedy
+ * SV_LMHEAD_ARGMAX.  Other bits: SV_ERR_DIMS.  Arguments otherwise as for sv_lmhead. */
+#define SV_LMHEAD_LOGITS 1
+#define SV_LMHEAD_ARGMAX 2
+SV_API sv_status sv_lmhead_ex(const uint16_t *hidden, const uint16_t *W_lmhead, sv_dims dims,
+                       int32_t flags, void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Stage 2 alone: softmax normalisers, accept tests, first rejection and the
  * replacement/bonus draw, from the logits and partials stage 1 left in the
  * same workspace, with the same dims, on the same device (stage 1 also

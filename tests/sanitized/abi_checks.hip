@@ -125,6 +125,10 @@ int main() {
                                        f<float>(), ok, f<int32_t>(), f<int32_t>(), F, ws,
                                        nullptr) == SV_ERR_DIMS);
     EXPECT(sv_debug_views(nullptr, ok, nullptr, nullptr, nullptr, nullptr) == SV_ERR_NULL);
+    for (int32_t flags : {4, 8, -1, INT32_MIN})
+        EXPECT(sv_lmhead_ex(f<uint16_t>(), f<uint16_t>(), ok, flags, F, ws, nullptr) == SV_ERR_DIMS);
+    EXPECT(sv_lmhead_ex(f<uint16_t>(), f<uint16_t>(), ok, SV_LMHEAD_LOGITS, F, ws - 1, nullptr) ==
+           SV_ERR_WORKSPACE);
 
     // the clustered head's dims
     const sv_head_dims hbad[] = {{0, 64, 100, 4, 25, 2}, {4, 12, 100, 4, 25, 2},

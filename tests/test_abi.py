@@ -309,3 +309,15 @@ def test_static_entry_point_errors_return_before_any_device_call():
     # the largest row counts the 48 MiB array holds at the two head shapes
     assert _lib.workspace_bytes(_lib.Dims(9, 4, 1536, 262144)) <= _lib.STATIC_SCRATCH_BYTES
     assert _lib.workspace_bytes(_lib.Dims(19, 4, 4096, 128256)) <= _lib.STATIC_SCRATCH_BYTES
+
+
+@no_device
+def test_lmhead_ex_flags():
+    lib = _lib.library()
+    p = ctypes.c_void_p(FAKE)
+    d = _lib.Dims(3, 4, 64, 1000)
+    ws = _lib.workspace_bytes(d)
+    assert lib.sv_lmhead_ex(p, p, d, 4, p, ws, None) == _lib.SV_ERR_DIMS
+    assert lib.sv_lmhead_ex(p, p, d, -1, p, ws, None) == _lib.SV_ERR_DIMS
+    assert lib.sv_lmhead_ex(p, p, d, 1, p, ws - 1, None) == _lib.SV_ERR_WORKSPACE
+    assert lib.sv_lmhead_ex(None, p, d, 3, p, ws, None) == _lib.SV_ERR_NULL

@@ -99,6 +99,37 @@ def test_stage_split_matches_whole_call():
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
+@pytest.mark.parametrize("B,gamma,d,V,seed", [(6, 4, 256, 3000, 11), (40, 7, 64, 5000, 12)])
+def test_lmhead_ex_split_matches_whole_calls(B, gamma, d, V, seed):
+    """sv_lmhead_ex with the logits only, then stage 2, is spec_verify bit for
+    bit; with the argmax partials only, then the greedy stage, it is
+    spec_verify_greedy (R = 30 and R = 320: both LM-head paths)."""
+    import torch
+    import draft_token_verification_02_amd as sv
+    dev = _dev()
+    _say(f"sv_lmhead_ex split B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    x = I.custom(B, gamma, d, V, seed=seed, w_std=parity.small_w_std(d))
+    whole = parity.run_gpu(x, dev)
+    t = parity.to_device(x, dev)
+    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    ws = sv.new_workspace(dims, dev)
+    out = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    n = torch.empty((B,), dtype=torch.int32, device=dev)
+    sv.lmhead(t["hidden_bits"], t["W_bits"], ws, argmax=False)
+    sv.accept_and_draw(dims, t["draft"], t["q"], t["uniforms"], out, n, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), whole["out"])
+    np.testing.assert_array_equal(n.cpu().numpy(), whole["n"])
+    np.testing.assert_array_equal(sv.debug_views(ws, dims)["logits"].cpu().numpy(), whole["logits"])
+    g_out, g_n, g_t = sv.verify_greedy(t["hidden_bits"], t["W_bits"], t["draft"])
+    tgt = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    sv.lmhead(t["hidden_bits"], t["W_bits"], ws, logits=False)
+    sv.accept_greedy(dims, t["draft"], out, n, ws, target_tokens=tgt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), g_out.cpu().numpy())
+    np.testing.assert_array_equal(tgt.cpu().numpy(), g_t.cpu().numpy())
+
+
 SWEEP = [f"sweep_b{b}_s{s}" for b in (16, 64, 256) for s in (0.2, 0.5, 1.0)]
 FULL = ["gemma_e2b", "llama8b_g2_b1", "llama8b_g4_b1", "llama8b_g8_b1", "llama8b_g2_b4",
         "llama8b_g4_b4", "llama8b_g8_b4", "sparse_q"] + SWEEP
