@@ -26,7 +26,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are device pointers owned by the caller.  The
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls (apart
+ *     from the static device array of spec_verify_static).
  *   - Work is enqueued on `hip_stream` (a hipStream_t passed as void*, NULL
  *     for the null stream) and is asynchronous: outputs are valid once the
  *     stream reaches that point.  No host synchronisation, no copies.
@@ -39,6 +40,31 @@
  *   - Shapes: B in [1, 2^20], gamma in [1, 32], d in [8, 65536] and a
  *     multiple of 8, V in [1, 2^28], and B * ceil(V / 4096) < 2^31.  `hidden`, `W`, `q` and `workspace`
  *     must be 16-byte aligned (workspace: 256-byte aligned).
+ *
+ * Precision (what a caller may rely on, and when it holds)
+ *   - Each logit is an fp32 sum of bf16 x bf16 products; the products are
+ *     exact in fp32, so a logit's error is summation rounding only:
+ *     |dl_j| <= gamma_{d-1} * sum_k |hidden[k] * W[j][k]|, with
+ *     gamma_n = n u / (1 - n u) and u = 2^-24, whatever the order of the
+ *     sum.  Rounding errors of random sign make the usual error far
+ *     smaller, about a quarter of 2^-24 * sqrt(d) * max_j |l_j| (measured
+ *     at d = 1536 with logits up to 90).
+ *   - With eps the largest |dl_j| of a row, every probability of that row
+ *     obeys |dp_j| <= p_j * (2 eps + 4e-6): the normaliser moves all p_j by
+ *     the p-weighted mean of the dl, and the exp2 and reciprocal steps add
+ *     under 2e-6 each.
+ *   - Hence |dp_j| <= 1e-5 for every entry whenever eps <= 3e-6, and for
+ *     every row whose largest p stays below 1e-5 / (2 eps + 4e-6) whatever
+ *     eps is.  On the usual error above, eps <= 3e-6 holds while
+ *     max_j |l_j| <= 200 / sqrt(d): logits up to about 3 at d = 4096 and 5
+ *     at d = 1536.  The guaranteed condition is the worst case:
+ *     gamma_{d-1} * max_j sum_k |hidden[k] W[j][k]| <= 3e-6.
+ *   - Decisions are taken on these fp32 values.  An accept test agrees with
+ *     the exact one unless its uniform lies within (2 eps + 4e-6) p/q of
+ *     p/q; a draw agrees unless u lies within 2 (2 eps + 4e-6) / S of an
+ *     edge of the normalised running sum (S the sum of the drawn weights).
+ *     Logits far beyond the scale above (say |l| ~ 100 at d = 4096) only
+ *     widen these bands; the results stay valid draws of fp32 arithmetic.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
