@@ -336,12 +336,11 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
         else:
             step_bytes = perfmodel.step_bytes(B, g, d, V, int((n_host < g).sum()))
         # R <= 64 rows: the streaming kernel, one launch per 64 rows; more
-        # rows: one launch of the pipelined 128-row GEMM (R <= 128) or of the
-        # ping-pong GEMM of 256-entry x 128-320-row blocks (when their
-        # partials fit, as in every named workload).
+        # rows: one launch of the ping-pong GEMM of 256-entry x 128-320-row
+        # blocks (when their partials fit, as in every named workload).
         tiled = R > 64 and -(-V // 256) <= 1024
         passes = 1 if tiled else -(-R // 64)
-        kernel = ("lmhead_mid_kernel" if R <= 128 else "lmhead_big_kernel") if tiled else "lmhead_kernel"
+        kernel = "lmhead_big_kernel" if tiled else "lmhead_kernel"
         if mode == "greedy":
             kernel += " + greedy_kernel"
     # Bound by whichever roofline takes longer for the algorithmic work.

@@ -59,14 +59,14 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (2, 3, 1536, 5000, 2),
     (5, 2, 72, 777, 3),
     (1, 1, 8, 1, 4),
-    (14, 4, 64, 4099, 5),      # R = 70: two row passes
+    (14, 4, 64, 4099, 5),      # R = 70: the tiled GEMM's 128-row blocks, three-stage ring
     (4, 8, 136, 300, 6),
     (2, 32, 40, 513, 7),       # gamma at its maximum
     (40, 7, 24, 65, 8),        # R = 320
     (1, 4, 4096, 2048, 9),
     (300, 1, 16, 33, 10),
-    (20, 4, 1024, 1000, 11),   # R = 100, the many-row GEMM's pipelined path, ragged V
-    (30, 4, 512, 2050, 12),    # R = 150: two row tiles, shortest pipelined d, V % 4 != 0
+    (20, 4, 1024, 1000, 11),   # R = 100, ragged V (a partial last vocab block)
+    (30, 4, 512, 2050, 12),    # R = 150: two 128-row blocks, four-stage ring, V % 4 != 0
     (1, 3, 16, 262143, 13),    # 64 chunks (one window of chunk totals), ragged last chunk
     (1, 4, 32, 300000, 14),    # 74 chunks: the split draw and the pick's multi-window search
     (2, 2, 24, 270001, 15),
@@ -75,8 +75,10 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (8, 4, 128, 3001, 17),     # R = 40, V % 4 != 0: per-element logit stores
     (12, 4, 512, 2048, 18),    # R = 60, four fragments
     (3, 7, 1536, 4096, 19),    # R = 24 at the Gemma-shaped d
-    (16, 5, 512, 3000, 20),    # R = 96: the 128-row GEMM's 96-row blocks, pipelined path
-    (49, 1, 512, 2003, 21),    # R = 98: its 128-row blocks, V % 4 != 0
+    (16, 5, 512, 3000, 20),    # R = 96
+    (49, 1, 512, 2003, 21),    # R = 98, V % 4 != 0
+    (13, 4, 200, 3000, 22),    # R = 65, d % 32 != 0: the ragged last k step
+    (25, 4, 1544, 1031, 23),   # R = 125 at d = 1544 (ragged k), V % 4 != 0
 ]
 
 
