@@ -76,6 +76,21 @@ def traffic_from_counters(cfg_name: str):
     return None
 
 
+def counter_calibration(cfg_name: str):
+    """How the committed counter summary of a workload turns counts into
+    bytes: the scales that make FETCH_SIZE and WRITE_SIZE read 1 GiB for a
+    1 GiB device copy, and the file they come from."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_counters.json"))):
+        with open(path) as f:
+            c = json.load(f)
+        if c.get("workload") == cfg_name:
+            return (f"FETCH_SIZE x {c['fetch_scale']:.3f} + WRITE_SIZE x {c['write_scale']:.3f} "
+                    f"(KiB per dispatch; scales from a {c['copy_probe_bytes'] >> 20} MiB device "
+                    f"copy), profiles/{os.path.basename(path)}")
+    return None
+
+
 def mfma_busy_from_counters(cfg_name: str):
     """Counter-based MFMA busy fraction of the tiled LM-head GEMM.
 
@@ -154,10 +169,11 @@ def cpu_baseline(x: dict, greedy: bool = False, gpu_value: float = None) -> dict
     positions/s on the whole batch."""
     B, g1, d = x["hidden_bits"].shape
     V = x["W_bits"].shape[0]
-    # samples sized for ~10 s of fp64 GEMM on a 16-core host / one core
+    # samples sized for ~3 s per run of fp64 GEMM on a 16-core host, ~2 s on
+    # one core (three runs each: ~15 s of host work in all)
     per_seq = 2.0 * g1 * d * V
-    s_all = max(1, min(B, int(3.0e11 / per_seq)))
-    s_one = max(1, min(B, int(2.0e10 / per_seq)))
+    s_all = max(1, min(B, int(1.0e12 / per_seq)))
+    s_one = max(1, min(B, int(4.0e10 / per_seq)))
     v_all, c_all, n_all, t_all = _oracle_rate(x, s_all, greedy, 30.0, None)
     v_one, c_one, n_one, t_one = _oracle_rate(x, s_one, greedy, 30.0, 1)
     res = {"value": v_all, "unit": "positions/s", "cores": c_all, "kind": "oracle",
@@ -355,6 +371,8 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
                 "peak": perfmodel.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] * 1e9 / perfmodel.MI355X_HBM_BYTES_PER_S
     roof["traffic"] = traffic_from_counters(cfg.name) if mode == "sample" else None
+    if roof["traffic"] is not None:
+        roof["traffic_calibration"] = counter_calibration(cfg.name)
     roof["alg_bytes_per_launch"] = lm_bytes // passes
     roof["hbm_GBps_alg"] = lm_bytes / lm_avg_s / 1e9
 

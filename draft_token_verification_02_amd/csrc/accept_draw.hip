@@ -176,10 +176,16 @@ __global__ __launch_bounds__(kDrawBlock) void accept_kernel(
 // writes its chunk totals, chunk 0's workgroup writes the outputs that
 // depend on n only, and pick_kernel follows (two launches, no device-scope
 // arrival per workgroup).  kDrawSplit: accept_kernel ran first; the
-// workgroup reads n and the draw row's normaliser it left and writes its
-// chunk totals, and pick_kernel follows.  A kernel boundary orders the
+// workgroup reads n and the draw row's normaliser it left and writes the
+// chunk totals of its split_chunks_per_group chunks, and pick_kernel follows.  A kernel boundary orders the
 // totals before the pick in both two-launch forms.
 enum DrawForm { kDrawSplit = 0, kDrawFused = 1, kDrawInline = 2 };
+// Chunks per workgroup in the split form (many sequences).  Dense q: four
+// 4096-token chunks in turn, a quarter of the workgroups (stage 2 at B = 256,
+// V = 128256: 63.2 -> 60.9 us; B = 64: 28.1 -> 27.1 us).  Sparse q: one,
+// since each chunk rebuilds its dense q from all K entries of the row (four
+// in turn measured 16.6 -> 23.4 us at B = 8).
+constexpr int split_chunks_per_group(bool sparse) { return sparse ? 1 : 4; }
 
 template <int FORM, bool SPARSE>
 __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
@@ -191,8 +197,12 @@ __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
     int32_t* __restrict__ status) {
     __shared__ float r_m[SV_MAX_GAMMA + 1], r_s[SV_MAX_GAMMA + 1];
     __shared__ __attribute__((aligned(16))) unsigned s_qc[SPARSE ? kDrawChunk : 4];
-    // flat grid: workgroup x covers chunk x % NC of sequence x / NC
-    const int c = (int)(blockIdx.x % (unsigned)NC), b = (int)(blockIdx.x / (unsigned)NC);
+    // flat grid: workgroup x covers chunks CPW (x % NG) .. CPW (x % NG) + CPW - 1
+    // of sequence x / NG, NG = ceil(NC / CPW) workgroups per sequence
+    constexpr int CPW = FORM == kDrawSplit ? split_chunks_per_group(SPARSE) : 1;
+    const int NG = (NC + CPW - 1) / CPW;
+    const int cg = (int)(blockIdx.x % (unsigned)NG), b = (int)(blockIdx.x / (unsigned)NG);
+    const int c = cg * CPW;                    // the first (with CPW = 1 the only) chunk
     const int g1 = gamma + 1;
 
     constexpr bool FUSED = FORM == kDrawFused;
@@ -211,15 +221,18 @@ __global__ __launch_bounds__(kDrawBlock) void draw_kernel(
         S = row_sum[(size_t)b * g1 + n];
     }
     const DrawRow d = draw_row<SPARSE>(logits, q, b, gamma, n, V, M, S);
-    const int c0 = c * kDrawChunk;
-    if (SPARSE && d.has_q()) stage_sparse_chunk(d, c0, s_qc);
-
-    float w[kDrawPerThread], p[kDrawPerThread];
-    draw_weights<SPARSE>(d, c0 + threadIdx.x * kDrawPerThread, s_qc, c0, w, p);
-    double tw = 0.0, tp = 0.0;
+    for (int i = 0; i < CPW && c + i < NC; ++i) {
+        const int c0 = (c + i) * kDrawChunk;
+        if (SPARSE && d.has_q()) stage_sparse_chunk(d, c0, s_qc);
+        float w[kDrawPerThread], p[kDrawPerThread];
+        draw_weights<SPARSE>(d, c0 + threadIdx.x * kDrawPerThread, s_qc, c0, w, p);
+        double tw = 0.0, tp = 0.0;
 #pragma unroll
-    for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
-    store_chunk_totals(tw, tp, cs, (size_t)b * NC + c);
+        for (int e = 0; e < kDrawPerThread; ++e) { tw += (double)w[e]; tp += (double)p[e]; }
+        store_chunk_totals(tw, tp, cs, (size_t)b * NC + c + i);
+        // the next chunk reuses the totals' and the sparse chunk's LDS
+        if (CPW > 1) __syncthreads();
+    }
     if (FORM == kDrawInline && c == 0) {       // the outputs that depend on n only
         if (threadIdx.x < g1) {
             const int i = threadIdx.x;
@@ -328,7 +341,9 @@ hipError_t launch_accept_draw_t(const float* logits, const float* part_max, cons
             out_tokens, n_accepted, status);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        draw_kernel<kDrawSplit, SPARSE><<<dim3(groups), dim3(kDrawBlock), 0, stream>>>(
+        constexpr int cpw = split_chunks_per_group(SPARSE);
+        const unsigned split_groups = (unsigned)((NC + cpw - 1) / cpw) * (unsigned)B;
+        draw_kernel<kDrawSplit, SPARSE><<<dim3(split_groups), dim3(kDrawBlock), 0, stream>>>(
             logits, part_max, part_sum, NP, NPs, draft, q, uniforms, gamma, V, NC, cs, counters,
             row_max, row_sum, out_tokens, n_accepted, status);
         e = hipGetLastError();
