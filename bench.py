@@ -412,6 +412,12 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
     if n_host is not None:
         res["emitted_tokens_per_s"] = float((n_host + 1).sum()) * K / elapsed
         res["n_accepted"] = n_host.tolist()[:16]
+        if mode in ("sample", "greedy", "sparse"):
+            # empirical acceptance rate: accepts over the accept tests the
+            # batch actually ran (checking stops at the first rejection)
+            tests = np.minimum(n_host + 1, g).sum()
+            res["alpha_empirical"] = float(n_host.sum()) / float(tests) if tests else None
+            res["mean_accepted_per_seq"] = float(n_host.mean())
     del t, ws
     torch.cuda.synchronize()
     return res, x
