@@ -145,8 +145,10 @@ __device__ __forceinline__ void read_frags_asm(u32x4 (&fa)[8], u32x4 (&fb)[FR], 
 #undef SV_DSR_A
 #undef SV_DSR
 
+// Two waves per SIMD (one workgroup per CU) with the four-stage ring; four
+// (two workgroups per CU: <= 128 registers) with the three-stage one.
 template <int FR, int S, bool ARG>
-__global__ __launch_bounds__(kBigNT) void lmhead_big_kernel(
+__global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ? 4 : 2))) void lmhead_big_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
     float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
