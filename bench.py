@@ -48,11 +48,38 @@ import perfmodel  # noqa: E402
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def code_text(src: str) -> str:
+    """C/C++/HIP source with its comments removed and whitespace runs folded
+    to one space (string and character literals kept as written), so that a
+    comment edit does not count as a change of the kernel."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(files) -> str:
+    """Hash of the code (comments and layout aside) of the given sources."""
     h = hashlib.sha256()
     for p in files:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -70,6 +70,7 @@ constexpr int kXcds = 8;
 // flight are filling, and waits for every copy (vmcnt(0)) once per ring
 // turn in each group; that wait exposed the full memory latency every S
 // steps (R = 128: 268 -> 251 us; R = 320: 402 -> 387 us).
+//
 // Stage layout: the 256 W rows, then the TR hidden rows, 64 bytes (32 bf16)
 // each; chunk g of row r sits in slot g ^ ((r >> 1) & 3), which rocprofv3's
 // SQ_LDS_BANK_CONFLICT counts as conflict-free for the fragment reads on
@@ -159,9 +160,8 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     static_assert(TV == kTV, "256 vocab rows per block: one softmax partial column each");
     static_assert(S == 3 || S == 4, "ring depth");
     static_assert(FV == 8 && kLmTile * kBigRowBytes == 1024, "fragment reads 1 KB apart");
-    // One array per stage, so that the compiler can tell the stage a
-    // fragment read uses from the stages copies are filling (with a single
-    // array it waits for every copy in flight before each read).
+    // One array per stage, each selected by a compile-time stage index in
+    // the unrolled loop (the fragment reads take them as LDS offsets).
     __shared__ __attribute__((aligned(1024))) char st0[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st1[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char st2[C::kStageBytes];

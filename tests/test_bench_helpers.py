@@ -52,3 +52,22 @@ def test_stale_summaries_are_ignored(tmp_path, monkeypatch):
     (tmp_path / "k.hip").write_text("kernel source, changed\n")
     assert bench.traffic_from_counters("w1") is None
     assert bench.mfma_busy_from_counters("w1") is None
+
+
+def test_comment_edits_keep_summaries_current(tmp_path, monkeypatch):
+    """A summary stays current through comment and layout edits of its
+    kernel's sources, and goes stale on a change of the code itself."""
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) { return x + 1; }  // one\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    h = bench.source_hash(["k.hip"])
+    _write(tmp_path, "a_counters.json", {"workload": "w1", "kernel_hash": h,
+                                         "kernel_sources": ["k.hip"],
+                                         "hbm_bytes_per_launch": 7.0})
+    src.write_text("/* a note */\nint f(int x) {\n    return x + 1;   // one, reworded\n}\n")
+    assert bench.traffic_from_counters("w1") == 7.0
+    src.write_text("int f(int x) { return x + 2; }  // one\n")
+    assert bench.traffic_from_counters("w1") is None
+    # comment markers inside string literals are code
+    assert bench.code_text('s = "a // b"; // c') == 's = "a // b";'
