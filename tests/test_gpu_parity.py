@@ -79,6 +79,9 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (49, 1, 512, 2003, 21),    # R = 98, V % 4 != 0
     (13, 4, 200, 3000, 22),    # R = 65, d % 32 != 0: the ragged last k step
     (25, 4, 1544, 1031, 23),   # R = 125 at d = 1544 (ragged k), V % 4 != 0
+    (43, 2, 200, 3000, 24),    # R = 129: 192-row blocks
+    (172, 4, 64, 700, 25),     # R = 860: 128-row blocks with the four-stage ring
+    (200, 4, 40, 900, 26),     # R = 1000: 256-row blocks, ragged k
 ]
 
 
