@@ -111,6 +111,8 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // address a, FR B fragments 1 KB apart from address b, then lgkmcnt(0) in
 // the same block, so every output register is written when the block ends.
 // Outputs are early-clobber: the two address registers stay live throughout.
+// The memory clobber keeps the block after the copies and barriers that make
+// the stage's bytes valid.
 #define SV_DSR(o, base, off) "ds_read_b128 %" #o ", %" #base " offset:" #off "\n"
 #define SV_DSR_A(base)                                                               \
     SV_DSR(0, base, 0) SV_DSR(1, base, 1024) SV_DSR(2, base, 2048) SV_DSR(3, base, 3072) \
@@ -125,21 +127,25 @@ __device__ __forceinline__ void read_frags_asm(u32x4 (&fa)[8], u32x4 (&fb)[FR], 
         asm volatile(SV_DSR_A(13) SV_DSR(8, 14, 0) SV_DSR(9, 14, 1024) SV_DSR(10, 14, 2048)
                      SV_DSR(11, 14, 3072) SV_DSR(12, 14, 4096) "s_waitcnt lgkmcnt(0)"
                      : SV_OUT_A, "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]), "=&v"(fb[3]), "=&v"(fb[4])
-                     : "v"(a), "v"(b));
+                     : "v"(a), "v"(b)
+                     : "memory");
     } else if constexpr (FR == 4) {
         asm volatile(SV_DSR_A(12) SV_DSR(8, 13, 0) SV_DSR(9, 13, 1024) SV_DSR(10, 13, 2048)
                      SV_DSR(11, 13, 3072) "s_waitcnt lgkmcnt(0)"
                      : SV_OUT_A, "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]), "=&v"(fb[3])
-                     : "v"(a), "v"(b));
+                     : "v"(a), "v"(b)
+                     : "memory");
     } else if constexpr (FR == 3) {
         asm volatile(SV_DSR_A(11) SV_DSR(8, 12, 0) SV_DSR(9, 12, 1024) SV_DSR(10, 12, 2048)
                      "s_waitcnt lgkmcnt(0)"
                      : SV_OUT_A, "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2])
-                     : "v"(a), "v"(b));
+                     : "v"(a), "v"(b)
+                     : "memory");
     } else {
         asm volatile(SV_DSR_A(10) SV_DSR(8, 11, 0) SV_DSR(9, 11, 1024) "s_waitcnt lgkmcnt(0)"
                      : SV_OUT_A, "=&v"(fb[0]), "=&v"(fb[1])
-                     : "v"(a), "v"(b));
+                     : "v"(a), "v"(b)
+                     : "memory");
     }
 }
 #undef SV_OUT_A
