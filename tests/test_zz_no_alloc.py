@@ -20,7 +20,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-CASES = [  # (B, gamma, d, V, seed), largest first; R > 64 takes the 128-row GEMM
+CASES = [  # (B, gamma, d, V, seed), largest first; R > 64 takes the tiled GEMM
     (16, 4, 512, 20000, 41),     # R = 80
     (4, 4, 256, 30000, 42),      # R = 20
     (2, 3, 128, 5000, 43),       # R = 8
