@@ -76,7 +76,8 @@ def test_tree_bad_tokens_are_rejected_and_flagged():
     assert gpu["status"][1] & 1 and gpu["status"][2] & 1
 
 
-@pytest.mark.parametrize("B,d,V,seed", [(1, 1536, 262144, 0), (4, 4096, 128256, 1)])
+@pytest.mark.parametrize("B,d,V,seed", [(1, 1536, 262144, 0), (4, 4096, 128256, 1),
+                                        (16, 4096, 128256, 2)])   # R = 104 and 416: tiled GEMM
 def test_tree_full_shape_parity(B, d, V, seed):
     dev = _dev()
     _say(f"tree full B={B} T={len(I.EAGLE_LIKE_TREE)} d={d} V={V} seed={seed}")
