@@ -66,7 +66,7 @@ SMALL = [  # (B, gamma, d, V, seed): tiles, ragged tails, V % 4 != 0, R > 64, sh
     (1, 4, 4096, 2048, 9),
     (300, 1, 16, 33, 10),
     (20, 4, 1024, 1000, 11),   # R = 100, ragged V (a partial last vocab block)
-    (30, 4, 512, 2050, 12),    # R = 150: two 128-row blocks, four-stage ring, V % 4 != 0
+    (30, 4, 512, 2050, 12),    # R = 150: one 192-row block, four-stage ring, V % 4 != 0
     (1, 3, 16, 262143, 13),    # 64 chunks (one window of chunk totals), ragged last chunk
     (1, 4, 32, 300000, 14),    # 74 chunks: the split draw and the pick's multi-window search
     (2, 2, 24, 270001, 15),
