@@ -17,16 +17,19 @@
 //      leading accepts, from a wave ballot;
 //   3. compute fp64 totals of the chunk's draw weights -- the residual
 //      max(0, p - q) at row n, or p at row gamma for the bonus -- and of p.
-// The last workgroup of the sequence to finish (a per-sequence counter that
-// the LM-head launch zeroes) scans the chunk totals, finds the chunk where
-// the running sum reaches u * S, rescans that chunk with the same code and
-// picks the first token that reaches it: an inverse CDF over ascending ids.
+// Then one wave scans the chunk totals, finds the chunk where the running sum
+// reaches u * S, then the wave of that chunk from its wave totals, rescans
+// that wave's tokens with the same code and picks the first token that
+// reaches it: an inverse CDF over ascending ids.
 //
-// Steps 1-2 run in one of two places.  With few draw workgroups every chunk
-// workgroup repeats them (they read (gamma+1) * NP * 8 bytes, little next to
-// the chunk) and the step needs no extra kernel boundary.  With many,
-// accept_kernel runs them once per sequence first and the chunk workgroups
-// read n and the draw row's normaliser from memory.
+// Three forms, by the number of draw workgroups.  Few: every chunk
+// workgroup runs steps 1-2 itself (they read (gamma+1) * NP * 8 bytes,
+// little next to the chunk) and the sequence's last workgroup to finish (a
+// per-sequence counter that the LM-head launch zeroes) picks: one launch.
+// More: the same, but pick_kernel picks (two launches).  Many: accept_kernel
+// runs steps 1-2 once per sequence, the chunk workgroups (four chunks each
+// with dense q) read n and the draw row's normaliser from memory, and
+// pick_kernel follows (three launches).
 //
 // q comes in one of two forms.  Dense: a full [V] row per drafted position.
 // Sparse: K (id, value) entries per row -- the drafter's clustered head
