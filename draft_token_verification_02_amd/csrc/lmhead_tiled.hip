@@ -43,26 +43,37 @@ constexpr int kXcds = 8;
 // Blocks of 256 vocab rows x TR = 64 FR hidden rows, eight waves in a
 // 2 (vocab) x 4 (rows) grid, each 128 vocab rows x 16 FR hidden rows
 // (8 x FR fragments).  Both operands go from memory straight into LDS
-// (global_load_lds_dwordx4: 16 bytes per lane, no registers on the way)
-// through a ring of S stages of one 32-wide k step each.
+// (buffer_load_dwordx4 ... lds or global_load_lds_dwordx4: 16 bytes per
+// lane, no registers on the way) through a ring of S stages of one 32-wide
+// k step each.
 //
 // Ping-pong.  Waves 0-3 (group A) and 4-7 (group B) share the SIMDs, one of
 // each per SIMD, and take turns: while one group issues its MFMAs for a k
 // step the other reads its next fragments from LDS, and two barriers per k
 // step (X, Y) swap the roles, so a SIMD's matrix unit always has a wave with
-// operands ready feeding it.  Each wave issues its share of the ring's
-// copies between its own MFMAs (one after each of the first fragment rows):
-// a copy that stalls in the memory pipeline then holds up only a wave whose
-// MFMAs already keep the matrix unit busy.  Per k step t:
+// operands ready feeding it.  Phase P_t runs from Y_{t-1} to X_t, Q_t from
+// X_t to Y_t.  Each copy instruction holds its wave ~30 cycles, so with the
+// four-stage ring (R > 128) a wave issues its share of the ring's copies in
+// its read phase, once its fragments have landed, where it would otherwise
+// wait at the next barrier; its MFMA phase is MFMAs only.  Per k step t:
+//   A: MFMAs(t) | wait own copies of t+1 | X | read frags(t+1), copies of t+S-1 | Y
+//   B: read frags(t), copies of t+S-1 | wait own copies of t+1 | X | MFMAs(t) | Y
+// With the three-stage ring (R <= 128, HBM-bound) that would leave group A
+// at most one phase to cover the memory latency, so there each wave issues
+// its copies between its own MFMAs instead (one after each of the first
+// fragment rows: the MFMAs already issued keep the matrix unit busy while
+// the copy waits):
 //   A: MFMAs(t) + copies of t+S-1 | wait own copies of t+1 | X | read frags(t+1) | Y
 //   B: read frags(t) | wait own copies of t+1 | X | MFMAs(t) + copies of t+S-1 | Y
 // Stage u % S holds step u.  Before X_t every wave has waited for its copies
 // of step t+1, so after X_t the stage of t+1 is whole (A reads it in Q_t, B
 // in P_{t+1}).  The copies of step t+S-1 go to stage (t-1) % S, which both
 // groups finished reading before step t began (A in Q_{t-2}, waited before
-// Y_{t-2}; B in P_{t-1}, waited before X_{t-1}).  Measured at R = 1280,
-// d = 4096 (per k step, s_memtime in a probe build): 40 MFMAs take ~680
-// cycles, a group's 13 fragment reads ~300-480.
+// Y_{t-2}; B in P_{t-1}, waited before X_{t-1}), and which no wave reads
+// during P_t or Q_t (A reads stage (t+1) % S, B stage t % S).  Measured at
+// R = 1280, d = 4096 (per k step, s_memtime in a probe build): a group's 40
+// MFMAs take ~650 cycles (~790 with copies between them), its 13 fragment
+// reads ~300; each barrier costs ~90-140 cycles.
 //
 // Fragment reads are one inline-asm block per k step (all reads, then the
 // lgkmcnt(0) wait, inside it).  Written as plain LDS loads, the compiler
@@ -100,6 +111,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 1 KB copy from memory into LDS through a buffer resource: lane i's 16
+// bytes from base + voff (a lane beyond the range's nbytes reads zeros) go to
+// lds + 16 i.  Records in bytes; 0x00020000 is the 32-bit data format any
+// raw buffer on gfx9 uses.
+__device__ __forceinline__ void buffer_copy_lds(const char* base, uint32_t nbytes, uint32_t voff,
+                                                __attribute__((address_space(3))) void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000), lds, 16,
+        voff, 0, 0, 0);
 }
 
 // LDS address (byte offset in the workgroup's LDS) of a __shared__ pointer.
@@ -154,7 +176,7 @@ __device__ __forceinline__ void read_frags_asm(u32x4 (&fa)[8], u32x4 (&fb)[FR], 
 
 // Two waves per SIMD (one workgroup per CU) with the four-stage ring; four
 // (two workgroups per CU: <= 128 registers) with the three-stage one.
-template <int FR, int S, bool ARG>
+template <int FR, int S, bool ARG, bool BUF>
 __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ? 4 : 2))) void lmhead_big_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
@@ -200,7 +222,18 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     // NI is not a multiple of NW a wave's last j may pass NI: it repeats its
     // previous copy (same bytes to the same place), so every wave issues NIW
     // copies per step and the vmcnt accounting is the same on every wave.
-    const uint16_t* src[NIW];
+    //
+    // BUF (both matrices under 4 GiB): each copy is a buffer load with the
+    // lane's byte offset from the matrix start fixed for the whole walk and
+    // the step's k in the resource base, so a copy costs scalar work, one
+    // M0 write and the load itself -- no per-lane address arithmetic, which
+    // as 64-bit pointer adds between the MFMAs held the MFMA phase back
+    // (R = 1280: 1179 -> 1120-1146 us).  The resource's range ends with the
+    // matrix, so a chunk past the end of the last row reads zeros.
+    // Otherwise: 64-bit pointers per copy.
+    const uint16_t* src[BUF ? 1 : NIW];
+    uint32_t voff[BUF ? NIW : 1];
+    bool from_w[NIW];
     int dst[NIW];
     // row = 16 j + lane / 4 with 16 j a multiple of 8, so (row >> 1) & 3 = (lane >> 3) & 3
     const int goff = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
@@ -208,8 +241,10 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     for (int m = 0; m < NIW; ++m) {
         const int j = wave + m * NW < NI ? wave + m * NW : wave + (m - 1) * NW;
         const int row = j * 16 + (lane >> 2);
-        src[m] = (row < TV ? W + (size_t)min(v0 + row, V - 1) * d
-                           : hidden + (size_t)min(r0 + row - TV, R - 1) * d) + goff;
+        const size_t elem = (row < TV ? (size_t)min(v0 + row, V - 1) : (size_t)min(r0 + row - TV, R - 1)) * d + goff;
+        from_w[m] = j < TV / 16;                 // the same for every lane of the instruction
+        if constexpr (BUF) voff[m] = (uint32_t)(elem * 2);
+        else src[m] = (row < TV ? W : hidden) + elem;
         dst[m] = j * 1024;
     }
 
@@ -220,14 +255,27 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     // step reads again, so that every step issues the same copies).  A chunk
     // past the end of a row copies the row's first chunk instead; the
     // fragment lanes holding it are zeroed after the read.
+    // With BUF the chunks past the end of a row read the next row's first
+    // bytes instead (or zeros past the matrix): the same fragment lanes are
+    // zeroed all the same.
     auto copy_k = [&](int t) {
         t = t < nk ? t : nk - 1;
         const int k0 = t * kBigK;
-        return (!ragged || k0 + goff < d) ? k0 : -goff;
+        return (BUF || !ragged || k0 + goff < d) ? k0 : -goff;
     };
+    // A buffer copy reads from the matrix at the step's k (base) up to the
+    // matrix's end (range): both uniform, so they live in scalar registers.
+    const uint32_t w_bytes = BUF ? (uint32_t)((size_t)V * d * 2) : 0u;
+    const uint32_t h_bytes = BUF ? (uint32_t)((size_t)R * d * 2) : 0u;
     auto copy_one = [&](int m, int kk, char* st) {
-        __builtin_amdgcn_global_load_lds(
-            (void*)(src[m] + kk), (__attribute__((address_space(3))) void*)(st + dst[m]), 16, 0, 0);
+        auto* l = (__attribute__((address_space(3))) void*)(st + dst[m]);
+        if constexpr (BUF) {
+            const uint32_t kb = (uint32_t)kk * 2u;
+            buffer_copy_lds(from_w[m] ? (const char*)W + kb : (const char*)hidden + kb,
+                            (from_w[m] ? w_bytes : h_bytes) - kb, voff[m], l);
+        } else {
+            __builtin_amdgcn_global_load_lds((void*)(src[m] + kk), l, 16, 0, 0);
+        }
     };
     auto copy = [&](int t, char* st) {
         const int kk = copy_k(t);
@@ -261,11 +309,11 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
             for (int b = 0; b < FR; ++b) fb[b] = u32x4{0u, 0u, 0u, 0u};
         }
     };
-    // The step's MFMAs, fragment row by fragment row, with this wave's copies
-    // of step t (into stage st) issued one after each of the first NIW rows:
-    // a copy that has to wait for the memory pipeline then stalls this wave
-    // while its MFMAs already issued keep the matrix unit busy.
+    // The step's MFMAs, fragment row by fragment row; with the three-stage
+    // ring this wave's copies of step t (into stage st) go one after each of
+    // the first NIW rows, with the four-stage ring into the read phase.
     static_assert(NIW <= FV, "one copy per fragment row at most");
+    constexpr bool kCopyInRead = S == 4;
     auto mfmas_copy = [&](int t, char* st) {
         const int kk = copy_k(t);
 #pragma unroll
@@ -275,19 +323,21 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, fa[a]), __builtin_bit_cast(bf16x8, fb[b]),
                     acc[a][b], 0, 0, 0);
-            if (a < NIW) copy_one(a, kk, st);
+            if (!kCopyInRead && a < NIW) copy_one(a, kk, st);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Each group issues its copies of step t+S-1 during its own MFMAs of
-    // step t, into stage (t-1) % S, which both groups finished reading before
-    // Y_{t-1} (A, in Q_{t-2}) and X_{t-1} (B, in P_{t-1}).  Before X_t each
-    // wave needs its copies of step t+1 complete: group A issued them in
-    // P_{t+2-S} and has issued those of steps t+2 .. t+S-1 after them (its
-    // MFMA phase of step t comes before X_t); group B issued them in
-    // Q_{t+2-S}, followed only by those of t+2 .. t+S-2.
-    constexpr int kWaitA = (S - 2) * NIW;
-    constexpr int kWaitB = (S - 3) * NIW;
+    // Each group issues its copies of step t+S-1 during step t, into stage
+    // (t-1) % S.  Before X_t each wave needs its copies of step t+1 complete
+    // (vmcnt counts in issue order); after them it has issued those of the
+    // later steps up to the last phase before X_t that carries copies.
+    // Copies in the read phase: A issued step t+1's in Q_{t+2-S}, then
+    // t+2 .. t+S-2 (S-3 sets); B in P_{t+2-S}, then t+2 .. t+S-1 (S-2
+    // sets, P_t included).  Copies in the MFMA phase: A in P_{t+2-S}, then
+    // t+2 .. t+S-1 (S-2 sets, P_t included); B in Q_{t+2-S}, then
+    // t+2 .. t+S-2 (S-3 sets).
+    constexpr int kWaitA = (kCopyInRead ? S - 3 : S - 2) * NIW;
+    constexpr int kWaitB = (kCopyInRead ? S - 2 : S - 3) * NIW;
     if (!group_b) {
         // Group A.  Prologue: copies of steps 0 .. S-2; step 0 whole; its fragments.
 #pragma unroll
@@ -307,6 +357,7 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
                 __builtin_amdgcn_sched_barrier(0);
                 read_frags(stage((h + 1) % S));                    // Q_t
                 finish_frags(t + 1);
+                if (kCopyInRead) copy(t + S - 1, stage((h + S - 1) % S));
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();                      // Y_t
                 __builtin_amdgcn_sched_barrier(0);
@@ -325,6 +376,7 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
                 if (t >= nk) break;
                 read_frags(stage(h));                              // P_t
                 finish_frags(t);
+                if (kCopyInRead) copy(t + S - 1, stage((h + S - 1) % S));
                 wait_vmcnt<kWaitB>();
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();                      // X_t
@@ -444,14 +496,21 @@ hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, int R, int d, i
     const int nrb = (R + C::TR - 1) / C::TR;
     const int nblocks = nvb * nrb;
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
-    if (part_arg)
-        lmhead_big_kernel<FR, S, true><<<dim3(grid), dim3(kBigNT), 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
-            n_counters);
+    // Buffer copies need both matrices' byte sizes to fit the 32-bit range.
+    const bool buf = (size_t)V * d * 2 < (1ull << 32) && (size_t)R * d * 2 < (1ull << 32);
+    const dim3 g(grid), blk(kBigNT);
+    if (part_arg && buf)
+        lmhead_big_kernel<FR, S, true, true><<<g, blk, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+    else if (part_arg)
+        lmhead_big_kernel<FR, S, true, false><<<g, blk, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+    else if (buf)
+        lmhead_big_kernel<FR, S, false, true><<<g, blk, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     else
-        lmhead_big_kernel<FR, S, false><<<dim3(grid), dim3(kBigNT), 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters,
-            n_counters);
+        lmhead_big_kernel<FR, S, false, false><<<g, blk, 0, stream>>>(
+            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     return hipGetLastError();
 }
 
