@@ -154,6 +154,65 @@ def test_full_config_parity(name):
     assert rep["seqs"] == cfg.B
 
 
+def test_lmhead_w_of_4gib_or_more():
+    """W at 4 GiB and over (262000 x 8200 bf16, 4.30 GB) is past the 32-bit
+    byte offsets of the many-row GEMM's buffer-load copies, so that launch
+    takes its 64-bit pointer copies instead.  Sampled logits against the
+    oracle's exact dot products -- the first and last rows of W (byte
+    offsets past 2^32), the partial last vocab block (262000 = 1023 * 256 +
+    112) and the ragged last k step (8200 = 256 * 32 + 8) included -- to the
+    stated fp32 summation bound, and each sampled row's normaliser against
+    the GPU's own logits."""
+    import torch
+    import draft_token_verification_02_amd as sv
+    dev = _dev()
+    B, gamma, d, V, seed = 16, 4, 8200, 262000, 91
+    assert V * d * 2 >= 1 << 32
+    _say(f"W of 4 GiB or more B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    g = torch.Generator(device=dev).manual_seed(seed)
+    W = torch.randn((V, d), generator=g, device=dev, dtype=torch.bfloat16).mul_(0.02)
+    hidden = torch.randn((B, gamma + 1, d), generator=g, device=dev, dtype=torch.bfloat16)
+    draft = torch.randint(0, V, (B, gamma), generator=g, device=dev, dtype=torch.int32)
+    q = torch.rand((B, gamma, V), generator=g, device=dev) + 0.5
+    q /= q.sum(dim=-1, keepdim=True)
+    u = torch.rand((B, gamma + 1), generator=g, device=dev).clamp_(min=1e-6)
+    dims = sv.dims_of(hidden, W)
+    ws = sv.new_workspace(dims, dev)
+    out, n = sv.verify(hidden, W, draft, q, u, workspace=ws)
+    torch.cuda.synchronize()
+    views = sv.debug_views(ws, dims)
+    R_ = B * (gamma + 1)
+    rows = [0, 1, 40, R_ - 1]
+    rng = np.random.default_rng(seed)
+    cols = sorted({0, 1, 255, 256, 131071, 200000, V - 112, V - 2, V - 1,
+                   *rng.integers(0, V, 8).tolist()})
+    h_bits = hidden.reshape(R_, d)[rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    w_bits = W[cols].view(torch.int16).cpu().numpy().view(np.uint16)
+    exact = R.lmhead_logits(h_bits, w_bits)
+    absdot = R.bf16_to_f64(h_bits).__abs__() @ R.bf16_to_f64(w_bits).__abs__().T
+    L = views["logits"][rows].double().cpu().numpy()
+    got = L[:, cols]
+    # the library's stated bound on a logit: an fp32 sum of exact bf16
+    # products in any order, gamma_{d-1} sum_k |h_k W_jk|
+    nu = (d - 1) * 2.0 ** -24
+    bound = nu / (1 - nu) * absdot
+    err = np.abs(got - exact)
+    _say(f"max |dlogit| {err.max():.3e}, largest allowed {bound.max():.3e}")
+    assert np.all(err <= bound), f"logit error {err.max()} beyond its bound"
+    for i, r in enumerate(rows):
+        m = L[i].max()
+        assert float(views["row_max"][r]) == m
+        s_ref = np.exp(L[i] - m).sum()
+        assert abs(float(views["row_sumexp"][r]) - s_ref) <= 2e-5 * s_ref
+    n_h = n.cpu().numpy()
+    o_h = out.cpu().numpy()
+    assert np.all((n_h >= 0) & (n_h <= gamma))
+    for b in range(B):
+        assert 0 <= o_h[b, n_h[b]] < V and np.all(o_h[b, n_h[b] + 1:] == -1)
+    assert np.all(views["status"].cpu().numpy() == 0)
+    del W, q, ws
+
+
 def test_large_logits_stated_bound():
     """Logits near 90 (W std 0.5, d = 1536), where fp32 accumulation alone moves
     p by more than 1e-5: the error chain the library documents, checked link by
