@@ -67,6 +67,15 @@ def test_workspace_bytes():
     assert _ws(1, 4, 64, 1000) % 256 == 0
 
 
+def test_static_workspace_limits_as_documented():
+    """The header's figures for the static workspace (48 MiB): gamma = 4 steps
+    of up to 45 rows at V = 262144 and 95 rows at V = 128256 fit, the next
+    batch size does not."""
+    lim = _lib.STATIC_SCRATCH_BYTES
+    assert _ws(9, 4, 1536, 262144) <= lim < _ws(10, 4, 1536, 262144)
+    assert _ws(19, 4, 4096, 128256) <= lim < _ws(20, 4, 4096, 128256)
+
+
 @no_device
 @pytest.mark.parametrize("dims", [(0, 4, 64, 100), (1, 0, 64, 100), (1, 33, 64, 100),
                                   (1, 4, 12, 100), (1, 4, 0, 100), (1, 4, 64, 0),
