@@ -1,8 +1,12 @@
 """spec_verify_static (the workspace in the library's static device array)
 against spec_verify with a caller workspace, through the C ABI, on an MI355X:
 the same outputs bit for bit on consecutive calls, each smaller than the one
-before, so that a call finds the array holding the previous call's data.
-Every case prints its shape before touching the GPU."""
+before, so that a call finds the array holding the previous call's data; and
+the call captured in a HIP graph (torch's graph capture on a side stream),
+every replay -- with eager work and synchronisations between them -- giving
+the eager call's outputs bit for bit: the library enqueues only kernels (no
+memset, copy or allocation).  Every case prints its shape before touching
+the GPU."""
 
 import sys
 
@@ -69,3 +73,37 @@ def test_static_workspace_rejects_dims_beyond_its_size():
     with pytest.raises(sv.SVError, match="more than the static"):
         sv.verify_static(h, W, draft, q, u)
     assert _lib.workspace_bytes(_lib.Dims(B, gamma, d, V)) > _lib.STATIC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("B, gamma, d, V, seed", [(4, 4, 256, 30000, 51), (16, 4, 512, 20000, 52)])
+def test_static_workspace_replays_in_a_graph(B, gamma, d, V, seed):
+    import torch
+    import draft_token_verification_02_amd as sv
+    assert torch.cuda.is_available(), "no ROCm device"
+    sv.library()
+    dev = torch.device("cuda:0")
+    _say(f"static workspace in a graph B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    x = I.custom(B, gamma, d, V, seed=seed, sigma=0.8, w_std=parity.small_w_std(d))
+    t = parity.to_device(x, dev)
+    args = (t["hidden_bits"], t["W_bits"], t["draft"], t["q"], t["uniforms"])
+    ref_out, ref_n = sv.verify_static(*args)          # eager; also resolves the array's address
+    torch.cuda.synchronize()
+    ref_out, ref_n = ref_out.cpu().numpy(), ref_n.cpu().numpy()
+    out = torch.full((B, gamma + 1), -7, dtype=torch.int32, device=dev)
+    n = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        sv.verify_static(*args, out_tokens=out, n_accepted=n)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(-7)                                 # eager work between the replays
+        n.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), ref_out, err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(n.cpu().numpy(), ref_n, err_msg=f"replay {rep}")
+    _say(f"graph replays ok: n={ref_n.tolist()}")
+    del graph, t
