@@ -118,24 +118,32 @@ def counter_calibration(cfg_name: str):
     return None
 
 
-def mfma_busy_from_counters(cfg_name: str):
-    """Counter-based MFMA busy fraction of the tiled LM-head GEMM.
+def mfma_counters(cfg_name: str) -> dict:
+    """Counter-based MFMA busy fraction of the tiled LM-head GEMM, and the
+    shader clock it ran at.
 
     From committed rocprofv3 runs (profiles/*_mfma_util.json: the
     derived MfmaUtil counter, MFMA busy cycles over active cycles of every
-    SIMD) of the default mode of one workload each; None when there is no
+    SIMD, and GRBM_GUI_ACTIVE per XCD over each dispatch's duration) of the
+    default mode of one workload each; None for both when there is no
     summary for this workload or the kernel's sources have changed since.
     """
     import glob
+    none = {"busy": None, "clock_ghz": None}
     for path in sorted(glob.glob(os.path.join(PROFILES, "*_mfma_util.json"))):
         with open(path) as f:
             c = json.load(f)
         if c.get("workload") != cfg_name:
             continue
         if c.get("kernel_hash") != source_hash(c.get("kernel_sources", [])):
-            return None
-        return c.get("mfma_util_pct") / 100.0
-    return None
+            return none
+        return {"busy": c.get("mfma_util_pct") / 100.0, "clock_ghz": c.get("shader_clock_ghz_median")}
+    return none
+
+
+def mfma_busy_from_counters(cfg_name: str):
+    """The counter-based MFMA busy fraction alone (see mfma_counters)."""
+    return mfma_counters(cfg_name)["busy"]
 
 
 def copy_bandwidth(dev, mib: int = 1024, reps: int = 5) -> float:
@@ -434,6 +442,7 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
         "lmhead_launches_per_step": passes,
         "mfma_frac": flops / lm_avg_s / perfmodel.MI355X_BF16_DENSE_FLOPS,
         "mfma_busy_frac_counters": mfma_busy_from_counters(cfg.name) if mode == "sample" else None,
+        "shader_clock_ghz_counters": mfma_counters(cfg.name)["clock_ghz"] if mode == "sample" else None,
         "roofline": roof,
     }
     if n_host is not None:
