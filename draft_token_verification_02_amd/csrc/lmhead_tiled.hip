@@ -17,8 +17,8 @@
 // both operands go from memory straight into LDS through a ring of k steps,
 // and the waves take turns between MFMAs and fragment reads (ping-pong).
 //
-//   R <= 128: FR = 2 with a three-stage ring -- 74 KB of LDS and <= 128
-//     registers, so two workgroups share a CU and one's loads, epilogue and
+//   R <= 128: FR = 2 with a three-stage ring -- 74 KB of LDS (76 KB with
+//     argmax partials) and <= 128 registers, so two workgroups share a CU and one's loads, epilogue and
 //     stores overlap the other's MFMAs.  HBM-bound: W is streamed once.
 //   R > 128: FR in {5, 4, 3, 2}, whichever pads R least (ties to the taller
 //     block), with a four-stage ring, one workgroup per CU.  At R = 1280 the
