@@ -224,9 +224,11 @@ def cpu_baseline(x: dict, greedy: bool = False, gpu_value: float = None) -> dict
     return res
 
 
-def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
+def measure(cfg, mode: str, steps: int, warmup: int, dev, w_layout: str = "rows") -> tuple:
     """Time ``steps`` whole steps of workload ``cfg`` in ``mode`` after
-    ``warmup`` untimed ones; returns (result dict, the host inputs)."""
+    ``warmup`` untimed ones; returns (result dict, the host inputs).
+    w_layout "tiled": the steps take W's SV_W_TILED copy, made once before
+    the timed regions (its time is reported, not counted in the steps)."""
     import numpy as np
     import torch
 
@@ -244,15 +246,34 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
 
     stream = torch.cuda.current_stream(dev)
     extra_cfg = {}
+    tile_ms = None
+    if w_layout == "tiled" and mode == "head":
+        raise SystemExit("--w-layout tiled: the drafter's head reads W row-major")
+
+    def lm_w(t):
+        """W as the verification calls take it; tiles it once for "tiled"."""
+        nonlocal tile_ms
+        if w_layout != "tiled":
+            return t["W_bits"]
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        Wt = sv.tile_w(t["W_bits"], stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        tile_ms = a.elapsed_time(b)
+        return Wt
+
     if mode == "tree":
         parent = inputs.EAGLE_LIKE_TREE
         x = inputs.tree_inputs(cfg.B, parent, cfg.d, cfg.V, w_std=cfg.w_std, sigma=cfg.sigma,
                                seed=cfg.seed)
         t = upload({k: v for k, v in x.items() if k != "parent"})
+        W = lm_w(t)
         T = len(parent)
         D, P, rounds = sv.tree_shape(parent)
         R = cfg.B * (T + 1)
-        dims = sv.Dims(cfg.B, T, cfg.d, cfg.V)
+        dims = sv.dims_of(t["hidden_bits"], W)
         ws = torch.empty(sv.tree_workspace_bytes(dims), dtype=torch.uint8, device=dev)
         out = torch.empty((cfg.B, D + 1), dtype=torch.int32, device=dev)
         n_acc = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
@@ -260,12 +281,12 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
         extra_cfg = {"tree_nodes": T, "tree_depth": D, "tree_rounds": rounds}
 
         def whole():
-            sv.verify_tree(t["hidden_bits"], t["W_bits"], parent, t["tokens"], t["q"],
+            sv.verify_tree(t["hidden_bits"], W, parent, t["tokens"], t["q"],
                            t["uniforms"], out_tokens=out, n_accepted=n_acc, path_nodes=path,
                            workspace=ws, stream=stream)
 
         def lm_only():
-            sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream, argmax=False)
+            sv.lmhead(t["hidden_bits"], W, ws, stream=stream, argmax=False)
     elif mode == "head":
         if cfg.sparse is None:
             raise SystemExit("--mode head needs a workload with clusters (e.g. --config sparse_q)")
@@ -295,8 +316,9 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
             del x["q"]
             extra_cfg = {"q_entries_per_row": int(ids.shape[-1])}
         t = upload(x)
+        W = lm_w(t)
         R = cfg.R
-        dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+        dims = sv.dims_of(t["hidden_bits"], W)
         ws = sv.new_workspace(dims, dev)
         out = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev)
         n_acc = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
@@ -304,11 +326,11 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
 
         def lm_only():
             if mode == "greedy":
-                sv.verify_greedy(t["hidden_bits"], t["W_bits"], t["draft"], out_tokens=out,
+                sv.verify_greedy(t["hidden_bits"], W, t["draft"], out_tokens=out,
                                  n_accepted=n_acc, target_tokens=tgt, workspace=ws, stream=stream)
             else:
                 # what spec_verify launches: logits kept, no argmax partials
-                sv.lmhead(t["hidden_bits"], t["W_bits"], ws, stream=stream, argmax=False)
+                sv.lmhead(t["hidden_bits"], W, ws, stream=stream, argmax=False)
 
         def stage2():
             if mode == "sample":
@@ -405,9 +427,11 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
         roof = {"bound": "hbm", "kernel": kernel, "achieved": lm_bytes / lm_avg_s / 1e9,
                 "peak": perfmodel.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] * 1e9 / perfmodel.MI355X_HBM_BYTES_PER_S
-    roof["traffic"] = traffic_from_counters(cfg.name) if mode == "sample" else None
+    # committed counter runs are keyed by workload, "+tiled_w" for the tiled W
+    prof_key = cfg.name + ("+tiled_w" if w_layout == "tiled" else "")
+    roof["traffic"] = traffic_from_counters(prof_key) if mode == "sample" else None
     if roof["traffic"] is not None:
-        roof["traffic_calibration"] = counter_calibration(cfg.name)
+        roof["traffic_calibration"] = counter_calibration(prof_key)
     roof["alg_bytes_per_launch"] = lm_bytes // passes
     roof["hbm_GBps_alg"] = lm_bytes / lm_avg_s / 1e9
 
@@ -431,9 +455,11 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
                    "tree": "; a 25-node draft tree, every node drawn from q at its parent",
                    "head": "; drafter hidden rows ~ N(0, 1), disjoint random clusters"}.get(mode, ""),
         "config": {"workload": f"{cfg.name}: LM head d={d} V={V}, gamma={g}, B={B}"
-                               + (f", {mode}" if mode != "sample" else ""),
+                               + (f", {mode}" if mode != "sample" else "")
+                               + (", W tiled" if w_layout == "tiled" else ""),
                    "B": B, "gamma": g, "d": d, "V": V, "sigma": cfg.sigma,
-                   "seed": cfg.seed, "rows": R, "parallelism": "single GPU", **extra_cfg},
+                   "seed": cfg.seed, "rows": R, "w_layout": w_layout if mode != "head" else "rows",
+                   "parallelism": "single GPU", **extra_cfg},
         "steps_per_s": K / elapsed,
         "step_alg_bytes": step_bytes,
         "step_GBps": step_bytes * K / elapsed / 1e9,
@@ -441,10 +467,12 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
         "lmhead_ms_avg": statistics.mean(lm_ms), "lmhead_ms_median": statistics.median(lm_ms),
         "lmhead_launches_per_step": passes,
         "mfma_frac": flops / lm_avg_s / perfmodel.MI355X_BF16_DENSE_FLOPS,
-        "mfma_busy_frac_counters": mfma_busy_from_counters(cfg.name) if mode == "sample" else None,
-        "shader_clock_ghz_counters": mfma_counters(cfg.name)["clock_ghz"] if mode == "sample" else None,
+        "mfma_busy_frac_counters": mfma_busy_from_counters(prof_key) if mode == "sample" else None,
+        "shader_clock_ghz_counters": mfma_counters(prof_key)["clock_ghz"] if mode == "sample" else None,
         "roofline": roof,
     }
+    if tile_ms is not None:
+        res["tile_w_ms_once"] = tile_ms
     if n_host is not None:
         res["emitted_tokens_per_s"] = float((n_host + 1).sum()) * K / elapsed
         res["n_accepted"] = n_host.tolist()[:16]
@@ -455,6 +483,8 @@ def measure(cfg, mode: str, steps: int, warmup: int, dev) -> tuple:
             res["alpha_empirical"] = float(n_host.sum()) / float(tests) if tests else None
             res["mean_accepted_per_seq"] = float(n_host.mean())
     del t, ws
+    if mode != "head":
+        del W
     torch.cuda.synchronize()
     return res, x
 
@@ -470,6 +500,9 @@ def main():
                          "('none' to skip)")
     ap.add_argument("--mode", choices=("sample", "greedy", "sparse", "tree", "head"),
                     default="sample")
+    ap.add_argument("--w-layout", choices=("rows", "tiled"), default="rows",
+                    help="W as the verification calls take it: [V][d] row-major, or its "
+                         "SV_W_TILED copy made once before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
@@ -494,10 +527,11 @@ def main():
 
     from synth import inputs
 
-    res, x = measure(inputs.CONFIGS[args.config], args.mode, args.steps, args.warmup, dev)
+    res, x = measure(inputs.CONFIGS[args.config], args.mode, args.steps, args.warmup, dev,
+                     args.w_layout)
     if args.extra_config != "none" and args.extra_config != args.config:
         ex, _ = measure(inputs.CONFIGS[args.extra_config], args.mode, args.steps, args.warmup,
-                        dev)
+                        dev, args.w_layout)
         keep = ("value", "unit", "ms_per_step", "steps_per_s", "step_GBps",
                 "step_frac_hbm_peak", "lmhead_ms_avg", "mfma_frac", "roofline", "config",
                 "emitted_tokens_per_s")

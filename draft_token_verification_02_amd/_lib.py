@@ -18,18 +18,19 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_OK, SV_ERR_NULL, SV_ERR_DIMS, SV_ERR_WORKSPACE, SV_ERR_ALIGN, SV_ERR_DEVICE = range(6)
 SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE, SV_DEV_BAD_QID = 1, 2, 4, 8
 SV_LMHEAD_LOGITS, SV_LMHEAD_ARGMAX = 1, 2
-ABI_VERSION = 4
+SV_W_ROWS, SV_W_TILED = 0, 1
+ABI_VERSION = 5
 STATIC_SCRATCH_BYTES = 48 << 20
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
            "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views",
            "spec_verify_sparse_q", "sv_accept_and_draw_sparse_q", "sv_sparse_head_workspace_bytes",
            "sv_sparse_head", "sv_tree_shape", "sv_tree_workspace_bytes", "spec_verify_tree",
-           "spec_verify_static", "sv_lmhead_ex")
+           "spec_verify_static", "sv_lmhead_ex", "sv_tiled_w_bytes", "sv_tile_w")
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("gamma", ctypes.c_int32), ("d", ctypes.c_int32),
-                ("V", ctypes.c_int32)]
+                ("V", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 class HeadDims(ctypes.Structure):
@@ -59,6 +60,10 @@ def _load():
         lib.sv_status_string.argtypes = [st]
         lib.sv_workspace_bytes.restype = sz
         lib.sv_workspace_bytes.argtypes = [Dims]
+        lib.sv_tiled_w_bytes.restype = sz
+        lib.sv_tiled_w_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        lib.sv_tile_w.restype = st
+        lib.sv_tile_w.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, sz, vp]
         lib.spec_verify.restype = st
         lib.spec_verify.argtypes = [vp, vp, vp, vp, vp, Dims, vp, vp, vp, sz, vp]
         lib.spec_verify_static.restype = st
@@ -103,9 +108,65 @@ def library():
     return _load()
 
 
+class TiledW:
+    """W [V, d] in the SV_W_TILED layout (1 KB tiles of 16 rows x 32 columns),
+    as sv_tile_w writes it.  Every entry point except sparse_head takes it in
+    place of the row-major W; its results are bitwise those of the row-major
+    form.  ``data`` is the tiled buffer (int16, sv_tiled_w_bytes / 2 entries)."""
+
+    def __init__(self, data, V: int, d: int):
+        self.data, self.V, self.d = data, int(V), int(d)
+
+    @property
+    def shape(self):
+        return (self.V, self.d)
+
+    @property
+    def device(self):
+        return self.data.device
+
+    @property
+    def dtype(self):
+        return self.data.dtype
+
+    def dim(self) -> int:
+        return 2
+
+    def is_contiguous(self) -> bool:
+        return self.data.is_contiguous()
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def tiled_w_bytes(V: int, d: int) -> int:
+    return int(_load().sv_tiled_w_bytes(V, d))
+
+
+def tile_w(W, *, out=None, stream=None) -> TiledW:
+    """sv_tile_w: the SV_W_TILED copy of the row-major W [V, d] (bf16 or int16
+    bits), written into ``out`` (int16, at least sv_tiled_w_bytes / 2 entries)
+    or a new tensor.  Done once per matrix; enqueued on the stream."""
+    import torch
+    if W.dim() != 2 or not W.is_contiguous() or W.dtype not in (torch.bfloat16, torch.int16,
+                                                                  torch.uint16):
+        raise ValueError("W must be a contiguous 2-D bf16/int16 tensor")
+    V, d = W.shape
+    n = tiled_w_bytes(V, d)
+    if n == 0:
+        raise SVError(SV_ERR_DIMS, "sv_tiled_w_bytes")
+    if out is None:
+        out = torch.empty(n // 2, dtype=torch.int16, device=W.device)
+    st = _load().sv_tile_w(_ptr(W), V, d, _ptr(out), out.numel() * out.element_size(),
+                           _stream_handle(W.device, stream))
+    if st != SV_OK:
+        raise SVError(st, "sv_tile_w")
+    return TiledW(out, V, d)
+
+
 def dims_of(hidden, W, draft=None) -> Dims:
     B, g1, d = hidden.shape
-    return Dims(B, g1 - 1, d, W.shape[0])
+    return Dims(B, g1 - 1, d, W.shape[0], SV_W_TILED if isinstance(W, TiledW) else SV_W_ROWS)
 
 
 def workspace_bytes(dims: Dims) -> int:
@@ -334,9 +395,12 @@ def sparse_head(h, W, centroids, members, k: int, *, q_ids=None, q_vals=None, cl
                 workspace=None, stream=None):
     """The drafter's clustered sparse head; returns (q_ids [N, k*M], q_vals [N, k*M], clusters [N, k]).
 
-    h bf16 [N, d]; W bf16 [V, d]; centroids bf16 [C, d]; members int32 [C, M].
+    h bf16 [N, d]; W bf16 [V, d] row-major (not a TiledW); centroids bf16 [C, d];
+    members int32 [C, M].
     """
     import torch
+    if isinstance(W, TiledW):
+        raise TypeError("sparse_head reads W row-major: pass the [V, d] tensor, not a TiledW")
     dev = W.device
     for name, t, dt in (("h", h, (torch.bfloat16, torch.int16, torch.uint16)),
                         ("W", W, (torch.bfloat16, torch.int16, torch.uint16)),
@@ -394,7 +458,7 @@ def verify_tree(hidden, W, parent, tokens, q, uniforms, *, out_tokens=None, n_ac
                 path_nodes=None, workspace=None, stream=None):
     """Tree verification; returns (out_tokens [B, D+1], n_accepted [B], path_nodes [B, D]).
 
-    hidden bf16 [B, T+1, d]; W bf16 [V, d]; parent host ints [T]; tokens int32
+    hidden bf16 [B, T+1, d]; W bf16 [V, d] or its TiledW; parent host ints [T]; tokens int32
     [B, T]; q float32 [B, P, V] (rows with children); uniforms float32 [B, T+1].
     """
     import torch
@@ -409,7 +473,7 @@ def verify_tree(hidden, W, parent, tokens, q, uniforms, *, out_tokens=None, n_ac
         raise ValueError(f"tokens must be contiguous int32 [{B}, {T1 - 1}]")
     if q.dtype != torch.float32 or tuple(q.shape) != (B, P, V) or not q.is_contiguous():
         raise ValueError(f"q must be contiguous float32 [{B}, {P}, {V}]")
-    dims = Dims(B, T1 - 1, d, V)
+    dims = dims_of(hidden, W)
     dev = W.device
     if out_tokens is None:
         out_tokens = torch.empty((B, D + 1), dtype=torch.int32, device=dev)

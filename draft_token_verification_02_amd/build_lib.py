@@ -6,8 +6,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["lmhead.hip", "lmhead_tiled.hip", "accept_draw.hip", "greedy.hip", "sparse_head.hip",
-           "tree.hip", "api.hip"]
+SOURCES = ["lmhead.hip", "lmhead_tiled.hip", "w_layout.hip", "accept_draw.hip", "greedy.hip",
+           "sparse_head.hip", "tree.hip", "api.hip"]
 OUT = os.path.join(HERE, "libspecverify.so")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

@@ -10,12 +10,15 @@
 
 namespace sv {
 int lmhead_grid(int V);
-hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                               float* logits, float* part_max, float* part_sum, int32_t* part_arg,
-                               int NPs, int32_t* counters, int n_counters, hipStream_t stream);
-hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                         float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, bool w_tiled, int R,
+                               int d, int V, float* logits, float* part_max, float* part_sum,
+                               int32_t* part_arg, int NPs, int32_t* counters, int n_counters,
+                               hipStream_t stream);
+hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, bool w_tiled, int R, int d,
+                         int V, float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                          int NPs, int grid, int32_t* counters, int n_counters, hipStream_t stream);
+size_t tiled_w_bytes(int V, int d);
+hipError_t launch_tile_w(const uint16_t* W, int V, int d, uint16_t* Wt, hipStream_t stream);
 hipError_t launch_greedy(const float* part_max, const int32_t* part_arg, int NP, int NPs, int B,
                          int gamma, int V, const int32_t* draft, int32_t* out_tokens,
                          int32_t* n_accepted, int32_t* target_tokens, int32_t* status,
@@ -40,9 +43,13 @@ hipError_t launch_tree(const float* logits, const float* part_max, const float* 
 
 namespace {
 
+bool w_shape_ok(int V, int d) { return d >= 8 && d <= 65536 && d % 8 == 0 && V >= 1 && V <= (1 << 28); }
+
+bool layout_ok(int32_t l) { return l == SV_W_ROWS || l == SV_W_TILED; }
+
 bool dims_ok(sv_dims d) {
-    if (!(d.B >= 1 && d.B <= (1 << 20) && d.gamma >= 1 && d.gamma <= SV_MAX_GAMMA && d.d >= 8 &&
-          d.d <= 65536 && d.d % 8 == 0 && d.V >= 1 && d.V <= (1 << 28)))
+    if (!(d.B >= 1 && d.B <= (1 << 20) && d.gamma >= 1 && d.gamma <= SV_MAX_GAMMA &&
+          w_shape_ok(d.V, d.d) && layout_ok(d.w_layout)))
         return false;
     // the draw's chunk-sum grid has one workgroup per (sequence, chunk)
     const int64_t chunks = (d.V + sv::kDrawChunk - 1) / sv::kDrawChunk;
@@ -74,14 +81,15 @@ sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* 
     const sv::Layout L = sv::make_layout(dims.B, dims.gamma, dims.d, dims.V);
     float* logits = keep_logits ? at<float>(ws, L.logits) : nullptr;
     int32_t* part_arg = with_argmax ? at<int32_t>(ws, L.part_arg) : nullptr;
+    const bool w_tiled = dims.w_layout == SV_W_TILED;
     hipError_t e;
     if (sv::lmhead_use_tiled(L.R, dims.V))
-        e = sv::launch_lmhead_tiled(hidden, W, L.R, dims.d, dims.V, logits,
+        e = sv::launch_lmhead_tiled(hidden, W, w_tiled, L.R, dims.d, dims.V, logits,
                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
                                     part_arg, L.NPs,
                                     at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
     else
-        e = sv::launch_lmhead(hidden, W, L.R, dims.d, dims.V, logits,
+        e = sv::launch_lmhead(hidden, W, w_tiled, L.R, dims.d, dims.V, logits,
                               at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
                               part_arg, L.NPs, sv::lmhead_grid(dims.V),
                               at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
@@ -156,7 +164,7 @@ bool head_dims_ok(sv_head_dims d) {
 
 bool tree_dims_ok(sv_dims d) {
     if (!(d.B >= 1 && d.B <= (1 << 20) && d.gamma >= 1 && d.gamma <= SV_MAX_TREE_NODES &&
-          d.d >= 8 && d.d <= 65536 && d.d % 8 == 0 && d.V >= 1 && d.V <= (1 << 28)))
+          w_shape_ok(d.V, d.d) && layout_ok(d.w_layout)))
         return false;
     const int64_t chunks = (d.V + sv::kDrawChunk - 1) / sv::kDrawChunk;
     return (int64_t)d.B * chunks <= INT32_MAX;
@@ -257,6 +265,21 @@ const char* sv_status_string(sv_status status) {
         case SV_ERR_DEVICE: return "SV_ERR_DEVICE: a HIP kernel launch failed";
     }
     return "unknown sv_status";
+}
+
+size_t sv_tiled_w_bytes(int32_t V, int32_t d) {
+    return w_shape_ok(V, d) ? sv::tiled_w_bytes(V, d) : 0;
+}
+
+sv_status sv_tile_w(const uint16_t* W, int32_t V, int32_t d, uint16_t* W_tiled, size_t tiled_bytes,
+                    void* hip_stream) {
+    if (!w_shape_ok(V, d)) return SV_ERR_DIMS;
+    if (!W || !W_tiled) return SV_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(W_tiled, 16)) return SV_ERR_ALIGN;
+    if (tiled_bytes < sv::tiled_w_bytes(V, d)) return SV_ERR_WORKSPACE;
+    return sv::launch_tile_w(W, V, d, W_tiled, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+               ? SV_OK
+               : SV_ERR_DEVICE;
 }
 
 size_t sv_workspace_bytes(sv_dims dims) {

@@ -83,7 +83,10 @@ __device__ __forceinline__ void quad_merge(float& m, float& s, float& av, int& a
     arg_merge(av, ai, av2, ai2);
 }
 
-template <int MT, int T, int U, bool FAST>
+// WT: W in 1 KB tiles of 16 vocab rows x 32 hidden columns (tile (i, t) at
+// element (i * nstep + t) * 512, rows within it 64 bytes apart), so a
+// fragment's k step is one contiguous 1 KB; otherwise [V][d] row-major.
+template <int MT, int T, int U, bool FAST, bool WT>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int row0, int rows,
     int d, int V, float* __restrict__ logits, float* __restrict__ part_max,
@@ -124,13 +127,16 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
 
     // Load cursor (group lg, k-step lk) with its fragment row pointers.
     // Rows past V are clamped to a valid row; their results are never kept.
+    // A lane's W chunk of k step lk is lp[t][lk * kWStep].
+    constexpr int kWStep = WT ? 64 : 4;      // 16-byte units between k steps of a row
     int lg = gb, lk = 0;
     const u32x4* lp[T];
     auto set_rows = [&](int g) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const int v = min((g * T + t) * kLmTile + r16, V - 1);
-            lp[t] = reinterpret_cast<const u32x4*>(W + (size_t)v * d) + kg;
+            const size_t row = WT ? (size_t)(v >> 4) * nstep * 512 + (v & 15) * 32 : (size_t)v * d;
+            lp[t] = reinterpret_cast<const u32x4*>(W + row) + kg;
         }
     };
     set_rows(lg);
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     auto load = [&](int slot) {
         if (FAST || lk * 32 + kg * 8 < d) {        // lanes past d load nothing
 #pragma unroll
-            for (int t = 0; t < T; ++t) wr[slot][t] = lp[t][lk * 4];
+            for (int t = 0; t < T; ++t) wr[slot][t] = lp[t][lk * kWStep];
 #pragma unroll
             for (int m = 0; m < MT; ++m) hr[slot][m] = hp[m][lk * 4];
         } else {
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
-                    for (int t = 0; t < T; ++t) wr[u][t] = lp[t][(lk + u) * 4];
+                    for (int t = 0; t < T; ++t) wr[u][t] = lp[t][(lk + u) * kWStep];
 #pragma unroll
                     for (int m = 0; m < MT; ++m) hr[u][m] = hp[m][(lk + u) * 4];
                 }
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 for (int u = 0; u < U; ++u) {
                     mma(u);
 #pragma unroll
-                    for (int t = 0; t < T; ++t) wr[u][t] = lp[t][(lk + u) * 4];
+                    for (int t = 0; t < T; ++t) wr[u][t] = lp[t][(lk + u) * kWStep];
 #pragma unroll
                     for (int m = 0; m < MT; ++m) hr[u][m] = hp[m][(lk + u) * 4];
                 }
@@ -459,16 +465,28 @@ int cu_count() {
     return n;
 }
 
-template <int MT>
+template <int MT, bool WT>
 void launch_mt(dim3 g, dim3 b, hipStream_t s, const uint16_t* hidden, const uint16_t* W, int row0,
                int rows, int d, int V, float* logits, float* pm, float* ps, int32_t* pa, int NPs,
                int32_t* counters, int nc) {
     constexpr int T = LmCfg<MT>::T, U = LmCfg<MT>::U;
     const int nstep = (d + 31) / 32;
     if (d % 32 == 0 && nstep % U == 0)
-        lmhead_kernel<MT, T, U, true><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc);
+        lmhead_kernel<MT, T, U, true, WT><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc);
     else
-        lmhead_kernel<MT, T, kGenericU, false><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc);
+        lmhead_kernel<MT, T, kGenericU, false, WT><<<g, b, 0, s>>>(hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc);
+}
+
+template <bool WT>
+void launch_rows(int mt, dim3 g, dim3 b, hipStream_t s, const uint16_t* hidden, const uint16_t* W,
+                 int row0, int rows, int d, int V, float* logits, float* pm, float* ps, int32_t* pa,
+                 int NPs, int32_t* counters, int nc) {
+    switch (mt) {
+        case 1: launch_mt<1, WT>(g, b, s, hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc); break;
+        case 2: launch_mt<2, WT>(g, b, s, hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc); break;
+        case 3: launch_mt<3, WT>(g, b, s, hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc); break;
+        default: launch_mt<4, WT>(g, b, s, hidden, W, row0, rows, d, V, logits, pm, ps, pa, NPs, counters, nc); break;
+    }
 }
 
 }  // namespace
@@ -489,21 +507,20 @@ int lmhead_grid(int V) {
 }
 
 // Enqueue the LM-head stage: one launch per group of up to 64 hidden rows.
-// logits may be null: then only the partials are written.
-hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
-                         float* logits, float* part_max, float* part_sum, int32_t* part_arg,
+// logits may be null: then only the partials are written.  w_tiled: W is in
+// the 16 x 32 tile layout, else [V][d] row-major.
+hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, bool w_tiled, int R, int d,
+                         int V, float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                          int NPs, int grid, int32_t* counters, int n_counters, hipStream_t stream) {
     for (int row0 = 0; row0 < R; row0 += kLmRowsPerPass) {
         const int rows = min(kLmRowsPerPass, R - row0);
         const int mt = (rows + kLmTile - 1) / kLmTile;
         const int nc = row0 == 0 ? n_counters : 0;
         dim3 g(grid), b(kLmWaves * kWave);
-        switch (mt) {
-            case 1: launch_mt<1>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            case 2: launch_mt<2>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            case 3: launch_mt<3>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-            default: launch_mt<4>(g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc); break;
-        }
+        if (w_tiled)
+            launch_rows<true>(mt, g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc);
+        else
+            launch_rows<false>(mt, g, b, stream, hidden, W, row0, rows, d, V, logits, part_max, part_sum, part_arg, NPs, counters, nc);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

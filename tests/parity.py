@@ -51,27 +51,34 @@ def to_device(x: dict, dev):
     return t
 
 
-def run_gpu(x: dict, dev, *, split=False):
-    """Run the step through the C ABI; return numpy outputs and debug views."""
+def gpu_w(t: dict, tiled: bool):
+    """The uploaded W as the entry points take it: row-major, or its tiled copy."""
+    import draft_token_verification_02_amd as sv
+    return sv.tile_w(t["W_bits"]) if tiled else t["W_bits"]
+
+
+def run_gpu(x: dict, dev, *, split=False, tiled=False):
+    """Run the step through the C ABI; return numpy outputs and debug views.
+    tiled: hand the entry points the SV_W_TILED copy of W."""
     import torch
     import draft_token_verification_02_amd as sv
     t = to_device(x, dev)
-    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    W = gpu_w(t, tiled)
+    dims = sv.dims_of(t["hidden_bits"], W)
     ws = sv.new_workspace(dims, dev)
     if split:
         out = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
         n = torch.empty((dims.B,), dtype=torch.int32, device=dev)
-        sv.lmhead(t["hidden_bits"], t["W_bits"], ws)
+        sv.lmhead(t["hidden_bits"], W, ws)
         sv.accept_and_draw(dims, t["draft"], t["q"], t["uniforms"], out, n, ws)
     else:
-        out, n = sv.verify(t["hidden_bits"], t["W_bits"], t["draft"], t["q"], t["uniforms"],
-                           workspace=ws)
+        out, n = sv.verify(t["hidden_bits"], W, t["draft"], t["q"], t["uniforms"], workspace=ws)
     torch.cuda.synchronize()
     v = sv.debug_views(ws, dims)
     res = {"out": out.cpu().numpy(), "n": n.cpu().numpy(),
            "logits": v["logits"].cpu().numpy(), "row_max": v["row_max"].cpu().numpy(),
            "row_sumexp": v["row_sumexp"].cpu().numpy(), "status": v["status"].cpu().numpy()}
-    del ws, t
+    del ws, t, W
     return res
 
 
@@ -210,27 +217,28 @@ def greedy_drafts(x: dict, ref_target: np.ndarray, p_match: float, seed: int) ->
     return np.where(take, ref_target[:, :g], x["draft"]).astype(np.int32)
 
 
-def run_gpu_greedy(x: dict, draft: np.ndarray, dev, *, split=False):
+def run_gpu_greedy(x: dict, draft: np.ndarray, dev, *, split=False, tiled=False):
     import torch
     import draft_token_verification_02_amd as sv
     t = to_device({"hidden_bits": x["hidden_bits"], "W_bits": x["W_bits"], "draft": draft}, dev)
-    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    W = gpu_w(t, tiled)
+    dims = sv.dims_of(t["hidden_bits"], W)
     ws = sv.new_workspace(dims, dev)
     res = {}
     if split:
         out = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
         n = torch.empty((dims.B,), dtype=torch.int32, device=dev)
         tgt = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
-        sv.lmhead(t["hidden_bits"], t["W_bits"], ws)
+        sv.lmhead(t["hidden_bits"], W, ws)
         sv.accept_greedy(dims, t["draft"], out, n, ws, target_tokens=tgt)
         torch.cuda.synchronize()
         res["logits"] = sv.debug_views(ws, dims)["logits"].cpu().numpy()
     else:
-        out, n, tgt = sv.verify_greedy(t["hidden_bits"], t["W_bits"], t["draft"], workspace=ws)
+        out, n, tgt = sv.verify_greedy(t["hidden_bits"], W, t["draft"], workspace=ws)
         torch.cuda.synchronize()
     res.update({"out": out.cpu().numpy(), "n": n.cpu().numpy(), "target": tgt.cpu().numpy(),
                 "status": sv.debug_views(ws, dims)["status"].cpu().numpy()})
-    del ws, t
+    del ws, t, W
     return res
 
 
@@ -306,14 +314,14 @@ def tree_parting_test(parent, tests_b, ref_path, gpu_path):
     raise AssertionError(f"the oracle never tested node {node}")
 
 
-def run_gpu_tree(x: dict, dev):
+def run_gpu_tree(x: dict, dev, *, tiled=False):
     import torch
     import draft_token_verification_02_amd as sv
     t = to_device({k: x[k] for k in ("hidden_bits", "W_bits", "tokens", "q", "uniforms")}, dev)
-    B, T1, d = x["hidden_bits"].shape
-    dims = sv.Dims(B, T1 - 1, d, x["W_bits"].shape[0])
+    W = gpu_w(t, tiled)
+    dims = sv.dims_of(t["hidden_bits"], W)
     ws = torch.empty(sv.tree_workspace_bytes(dims), dtype=torch.uint8, device=dev)
-    out, n, path = sv.verify_tree(t["hidden_bits"], t["W_bits"], x["parent"], t["tokens"], t["q"],
+    out, n, path = sv.verify_tree(t["hidden_bits"], W, x["parent"], t["tokens"], t["q"],
                                   t["uniforms"], workspace=ws)
     torch.cuda.synchronize()
     v = sv.debug_views(ws, dims)

@@ -28,7 +28,7 @@ void expect(bool ok, const char* what, int line) {
 void* const F = reinterpret_cast<void*>(uintptr_t(1) << 40);
 template <typename T> T* f() { return static_cast<T*>(F); }
 
-sv_dims D(int B, int g, int d, int V) { return sv_dims{B, g, d, V}; }
+sv_dims D(int B, int g, int d, int V, int layout = SV_W_ROWS) { return sv_dims{B, g, d, V, layout}; }
 
 // Reference tree check: parent[t] in [-1, t); depth of the deepest node;
 // rows with children.
@@ -61,7 +61,8 @@ int main() {
                            D(1, 4, 0, 100), D(1, 4, 64, 0), D(1, 4, 64, (1 << 28) + 1),
                            D((1 << 20) + 1, 1, 8, 1), D(1, 4, 65544, 10), D(-1, 4, 64, 100),
                            D(1 << 20, 32, 8, 1 << 28), D(INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX),
-                           D(INT32_MIN, 4, 64, 100)};
+                           D(INT32_MIN, 4, 64, 100), D(1, 4, 64, 100, 2), D(1, 4, 64, 100, -1),
+                           D(1, 4, 64, 100, INT32_MIN)};
     for (const sv_dims& d : bad) {
         EXPECT(sv_workspace_bytes(d) == 0);
         EXPECT(spec_verify(f<uint16_t>(), f<uint16_t>(), f<int32_t>(), f<float>(), f<float>(), d,
@@ -79,7 +80,8 @@ int main() {
                                     big, nullptr) == SV_ERR_DIMS);
     }
     const sv_dims large[] = {D(32767, 32, 65536, 1 << 28), D(1 << 20, 32, 65536, 4096),
-                             D(1, 1, 8, 1), D(256, 4, 4096, 128256)};
+                             D(1, 1, 8, 1), D(256, 4, 4096, 128256),
+                             D(32767, 32, 65536, 1 << 28, SV_W_TILED)};
     for (const sv_dims& d : large) {
         const size_t w = sv_workspace_bytes(d);
         const size_t R = (size_t)d.B * (d.gamma + 1);
@@ -89,6 +91,18 @@ int main() {
         EXPECT(sv_debug_views(F, d, &lg, &mx, &sm, &st) == SV_OK);
         EXPECT(lg == F && (const char*)st + 4 * (size_t)d.B <= (const char*)F + w);
     }
+
+    // the tiled W form: sizes at the extremes, argument errors
+    EXPECT(sv_tiled_w_bytes(1 << 28, 65536) == ((size_t)1 << 24) * 2048 * 1024);
+    EXPECT(sv_tiled_w_bytes(1, 8) == 1024 && sv_tiled_w_bytes(17, 40) == 4096);
+    EXPECT(sv_tiled_w_bytes(0, 64) == 0 && sv_tiled_w_bytes(10, 12) == 0 &&
+           sv_tiled_w_bytes(INT32_MAX, INT32_MAX) == 0 && sv_tiled_w_bytes(INT32_MIN, 64) == 0);
+    EXPECT(sv_tile_w(f<uint16_t>(), (1 << 28) + 1, 64, f<uint16_t>(), big, nullptr) == SV_ERR_DIMS);
+    EXPECT(sv_tile_w(nullptr, 100, 64, f<uint16_t>(), big, nullptr) == SV_ERR_NULL);
+    EXPECT(sv_tile_w(f<uint16_t>(), 100, 64, nullptr, big, nullptr) == SV_ERR_NULL);
+    EXPECT(sv_tile_w(f<uint16_t>() + 4, 100, 64, f<uint16_t>(), big, nullptr) == SV_ERR_ALIGN);
+    EXPECT(sv_tile_w(f<uint16_t>(), 100, 64, f<uint16_t>(), sv_tiled_w_bytes(100, 64) - 1,
+                     nullptr) == SV_ERR_WORKSPACE);
 
     // every pointer argument NULL in turn, misalignment, short workspace
     const sv_dims ok = D(3, 4, 64, 1000);

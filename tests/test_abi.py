@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for name in _declared():
         assert hasattr(raw, name), name
-    assert lib.sv_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.sv_abi_version() == _lib.ABI_VERSION == 5
 
 
 def test_status_strings():
@@ -80,7 +80,8 @@ def test_static_workspace_limits_as_documented():
 @pytest.mark.parametrize("dims", [(0, 4, 64, 100), (1, 0, 64, 100), (1, 33, 64, 100),
                                   (1, 4, 12, 100), (1, 4, 0, 100), (1, 4, 64, 0),
                                   (1, 4, 64, (1 << 28) + 1), ((1 << 20) + 1, 1, 8, 1),
-                                  (1, 4, 65544, 10), (-1, 4, 64, 100)])
+                                  (1, 4, 65544, 10), (-1, 4, 64, 100), (1, 4, 64, 100, 2),
+                                  (1, 4, 64, 100, -1)])
 def test_invalid_dims(dims):
     d = _lib.Dims(*dims)
     assert _lib.workspace_bytes(d) == 0
@@ -97,6 +98,41 @@ def test_invalid_dims(dims):
     # the views also serve tree calls, whose gamma (T) may reach SV_MAX_TREE_NODES
     want = _lib.SV_ERR_DIMS if _lib.tree_workspace_bytes(d) == 0 else _lib.SV_OK
     assert lib.sv_debug_views(p, d, ctypes.byref(out), None, None, None) == want
+
+
+def test_tiled_w_bytes():
+    """16 ceil(V / 16) rows x 32 ceil(d / 32) columns of bf16; 0 outside the
+    shape limits of sv_dims."""
+    assert _lib.tiled_w_bytes(1, 8) == 16 * 32 * 2
+    assert _lib.tiled_w_bytes(17, 40) == 32 * 64 * 2
+    assert _lib.tiled_w_bytes(128256, 4096) == 128256 * 4096 * 2
+    assert _lib.tiled_w_bytes(262143, 1544) == 262144 * 1568 * 2
+    for V, d in ((0, 64), (10, 0), (10, 12), (10, 65544), ((1 << 28) + 1, 8)):
+        assert _lib.tiled_w_bytes(V, d) == 0
+
+
+def test_layout_does_not_change_workspace():
+    for dims in ((1, 4, 1536, 262144), (64, 4, 4096, 128256), (3, 2, 40, 1000)):
+        assert _lib.workspace_bytes(_lib.Dims(*dims, _lib.SV_W_TILED)) == _ws(*dims) > 0
+
+
+def test_sparse_head_refuses_a_tiled_w():
+    with pytest.raises(TypeError):
+        _lib.sparse_head(None, _lib.TiledW(None, 1000, 64), None, None, 2)
+
+
+@no_device
+def test_tile_w_argument_errors():
+    lib = _lib.library()
+    p = ctypes.c_void_p(FAKE)
+    n = _lib.tiled_w_bytes(100, 64)
+    assert lib.sv_tile_w(p, 100, 12, p, n, None) == _lib.SV_ERR_DIMS
+    assert lib.sv_tile_w(p, 0, 64, p, n, None) == _lib.SV_ERR_DIMS
+    assert lib.sv_tile_w(None, 100, 64, p, n, None) == _lib.SV_ERR_NULL
+    assert lib.sv_tile_w(p, 100, 64, None, n, None) == _lib.SV_ERR_NULL
+    assert lib.sv_tile_w(ctypes.c_void_p(FAKE + 8), 100, 64, p, n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_tile_w(p, 100, 64, ctypes.c_void_p(FAKE + 2), n, None) == _lib.SV_ERR_ALIGN
+    assert lib.sv_tile_w(p, 100, 64, p, n - 1, None) == _lib.SV_ERR_WORKSPACE
 
 
 @no_device
@@ -271,6 +307,8 @@ def test_tree_workspace_bytes():
     assert _lib.tree_workspace_bytes(_lib.Dims(2, 64, 64, 100)) > 0
     assert _lib.tree_workspace_bytes(_lib.Dims(2, 65, 64, 100)) == 0
     assert _lib.tree_workspace_bytes(_lib.Dims(0, 4, 64, 100)) == 0
+    assert _lib.tree_workspace_bytes(_lib.Dims(2, 4, 64, 100, 2)) == 0
+    assert _lib.tree_workspace_bytes(_lib.Dims(2, 4, 64, 100, _lib.SV_W_TILED)) > 0
 
 
 @no_device

@@ -43,21 +43,22 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def run_gpu_sparse(x: dict, ids: np.ndarray, vals: np.ndarray, dev, *, split=False):
+def run_gpu_sparse(x: dict, ids: np.ndarray, vals: np.ndarray, dev, *, split=False, tiled=False):
     import torch
     import draft_token_verification_02_amd as sv
     t = parity.to_device({"hidden_bits": x["hidden_bits"], "W_bits": x["W_bits"],
                           "draft": x["draft"], "uniforms": x["uniforms"], "ids": ids,
                           "vals": vals}, dev)
-    dims = sv.dims_of(t["hidden_bits"], t["W_bits"])
+    W = parity.gpu_w(t, tiled)
+    dims = sv.dims_of(t["hidden_bits"], W)
     ws = sv.new_workspace(dims, dev)
     if split:
         out = torch.empty((dims.B, dims.gamma + 1), dtype=torch.int32, device=dev)
         n = torch.empty((dims.B,), dtype=torch.int32, device=dev)
-        sv.lmhead(t["hidden_bits"], t["W_bits"], ws)
+        sv.lmhead(t["hidden_bits"], W, ws)
         sv.accept_and_draw_sparse_q(dims, t["draft"], t["ids"], t["vals"], t["uniforms"], out, n, ws)
     else:
-        out, n = sv.verify_sparse_q(t["hidden_bits"], t["W_bits"], t["draft"], t["ids"], t["vals"],
+        out, n = sv.verify_sparse_q(t["hidden_bits"], W, t["draft"], t["ids"], t["vals"],
                                     t["uniforms"], workspace=ws)
     torch.cuda.synchronize()
     v = sv.debug_views(ws, dims)

@@ -1,0 +1,197 @@
+"""The tiled layout of W (SV_W_TILED) on an MI355X, through the C ABI.
+
+  * sv_tile_w writes exactly the documented layout: bit for bit against the
+    tiles cut out of W on the host (a reshape and zero padding, no
+    arithmetic);
+  * every entry point that takes sv_dims gives bitwise the results of the
+    row-major form of the same W -- the GEMM reads the same values in the
+    same order -- at row counts that reach every LM-head kernel form (R <= 64
+    in one to four hidden fragments, 64 < R <= 128, and the 192-, 256-, 320-
+    and 128-row blocks above), with V and d ragged against the tiles and the
+    k step, at the workloads' full shapes, and with the tiled copy past 4 GiB;
+  * each verification mode meets the oracle directly with the tiled W too.
+
+Every case prints its name, seed and shape before touching the GPU.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from synth import inputs as I
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("out", "n", "logits", "row_max", "row_sumexp", "status")
+
+
+def _dev():
+    import torch
+    assert torch.cuda.is_available(), "no ROCm device"
+    import draft_token_verification_02_amd as sv
+    sv.library()
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def host_tiles(w_bits: np.ndarray) -> np.ndarray:
+    """The documented layout, cut out of W [V][d] on the host: rows padded to
+    a multiple of 16 and columns to a multiple of 32 with zeros, then tile
+    (i, t) = rows 16 i .. 16 i + 15 x columns 32 t .. 32 t + 31, tiles in
+    (i, t) order, each row-major."""
+    V, d = w_bits.shape
+    Vp, dp = -(-V // 16) * 16, -(-d // 32) * 32
+    p = np.zeros((Vp, dp), dtype=np.uint16)
+    p[:V, :d] = w_bits
+    return p.reshape(Vp // 16, 16, dp // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("V,d,seed", [(1, 8, 1), (17, 40, 2), (3001, 200, 3), (4096, 256, 4),
+                                      (262144, 1536, 5)])
+def test_tile_w_writes_the_documented_layout(V, d, seed):
+    import torch
+    import draft_token_verification_02_amd as sv
+    dev = _dev()
+    _say(f"tile_w layout V={V} d={d} seed={seed}")
+    rng = np.random.default_rng(seed)
+    w = rng.integers(0, 1 << 16, (V, d), dtype=np.uint16)      # any bits: a pure copy
+    W = torch.from_numpy(w.view(np.int16)).to(dev)
+    out = torch.full((sv.tiled_w_bytes(V, d) // 2 + 64,), -1, dtype=torch.int16, device=dev)
+    t = sv.tile_w(W, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    n = sv.tiled_w_bytes(V, d) // 2
+    np.testing.assert_array_equal(got[:n], host_tiles(w))
+    assert np.all(got[n:] == 0xFFFF), "wrote past sv_tiled_w_bytes"
+    assert t.shape == (V, d) and t.data_ptr() == out.data_ptr()
+
+
+# (B, gamma, d, V, seed): R = B (gamma + 1) picks the kernel form
+CASES = [
+    (1, 4, 200, 3001, 11),      # R = 5: one hidden fragment; d ragged (200 = 6 * 32 + 8), V % 16 = 9
+    (4, 4, 256, 3001, 12),      # R = 20: two fragments, d a whole number of ring blocks
+    (8, 4, 72, 2000, 13),       # R = 40: three fragments, the ragged-d loop
+    (12, 4, 256, 1500, 14),     # R = 60: four fragments
+    (16, 4, 200, 3001, 15),     # R = 80: 128-row blocks, three-stage ring, ragged d
+    (25, 4, 256, 3001, 16),     # R = 125
+    (32, 4, 136, 2600, 17),     # R = 160: 192-row blocks
+    (40, 4, 256, 1000, 18),     # R = 200: 256-row blocks
+    (64, 4, 256, 3001, 19),     # R = 320: one 320-row block
+    (280, 4, 64, 700, 20),      # R = 1400: 128-row blocks, four-stage ring
+]
+
+
+@pytest.mark.parametrize("B,gamma,d,V,seed", CASES)
+def test_tiled_w_is_bitwise_the_row_major_result(B, gamma, d, V, seed):
+    dev = _dev()
+    _say(f"tiled vs row-major B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    x = I.custom(B, gamma, d, V, seed=seed, sigma=0.8, w_std=parity.small_w_std(d))
+    for split in (False, True):
+        rows = parity.run_gpu(x, dev, split=split)
+        tiled = parity.run_gpu(x, dev, split=split, tiled=True)
+        for k in KEYS:
+            np.testing.assert_array_equal(tiled[k], rows[k], err_msg=f"{k} split={split}")
+    draft = x["draft"]
+    rows = parity.run_gpu_greedy(x, draft, dev, split=True)
+    tiled = parity.run_gpu_greedy(x, draft, dev, split=True, tiled=True)
+    for k in ("out", "n", "target", "logits", "status"):
+        np.testing.assert_array_equal(tiled[k], rows[k], err_msg=f"greedy {k}")
+
+
+@pytest.mark.parametrize("B,gamma,d,V,seed", [CASES[0], CASES[4], CASES[6]])
+def test_tiled_w_meets_the_oracle(B, gamma, d, V, seed):
+    dev = _dev()
+    _say(f"tiled vs oracle B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    x = I.custom(B, gamma, d, V, seed=seed, sigma=0.8, w_std=parity.small_w_std(d))
+    rep = parity.compare(x, parity.run_gpu(x, dev, tiled=True))
+    _say("tiled sample mode", rep)
+    from oracle import greedy_ref as G
+    ref = G.verify_greedy(x["hidden_bits"], x["W_bits"], x["draft"])
+    draft = parity.greedy_drafts(x, ref.target, 0.7, seed)
+    ref = G.verify_greedy(x["hidden_bits"], x["W_bits"], draft)
+    rep = parity.compare_greedy(x, draft, parity.run_gpu_greedy(x, draft, dev, tiled=True), ref)
+    _say("tiled greedy mode", rep)
+
+
+def test_tiled_w_tree_and_sparse_q():
+    dev = _dev()
+    _say("tiled tree B=3 d=200 V=3001 seed=21; sparse q B=4 gamma=4 d=136 V=5000 seed=22")
+    xt = I.tree_inputs(3, I.EAGLE_LIKE_TREE, 200, 3001, seed=21, sigma=0.8,
+                       w_std=parity.small_w_std(200))
+    rows = parity.run_gpu_tree(xt, dev)
+    tiled = parity.run_gpu_tree(xt, dev, tiled=True)
+    for k in KEYS + ("path",):
+        np.testing.assert_array_equal(tiled[k], rows[k], err_msg=f"tree {k}")
+    _say("tiled tree", parity.compare_tree(xt, tiled))
+    from tests.test_gpu_sparse import run_gpu_sparse
+    xs = I.truncate_q(I.custom(4, 4, 136, 5000, seed=22, sigma=0.8,
+                               w_std=parity.small_w_std(136)), 200, 122)
+    ids, vals = I.to_sparse_q(xs["q"], pad=2, shuffle_seed=22)
+    rows = run_gpu_sparse(xs, ids, vals, dev)
+    tiled = run_gpu_sparse(xs, ids, vals, dev, tiled=True)
+    for k in KEYS:
+        np.testing.assert_array_equal(tiled[k], rows[k], err_msg=f"sparse q {k}")
+    _say("tiled sparse q", parity.compare(xs, tiled))
+
+
+def _full_shape_pair(B, gamma, d, V, seed, dev, *, static=False):
+    """verify() on the row-major W and on its tiled copy (inputs drawn on the
+    GPU); every output and debug view must agree bit for bit."""
+    import torch
+    import draft_token_verification_02_amd as sv
+    g = torch.Generator(device=dev).manual_seed(seed)
+    W = torch.randn((V, d), generator=g, device=dev, dtype=torch.bfloat16).mul_(0.02)
+    hidden = torch.randn((B, gamma + 1, d), generator=g, device=dev, dtype=torch.bfloat16)
+    draft = torch.randint(0, V, (B, gamma), generator=g, device=dev, dtype=torch.int32)
+    q = torch.rand((B, gamma, V), generator=g, device=dev) + 0.5
+    q /= q.sum(dim=-1, keepdim=True)
+    u = torch.rand((B, gamma + 1), generator=g, device=dev).clamp_(min=1e-6)
+    Wt = sv.tile_w(W)
+    res = []
+    for w in (W, Wt):
+        dims = sv.dims_of(hidden, w)
+        ws = sv.new_workspace(dims, dev)
+        out, n = sv.verify(hidden, w, draft, q, u, workspace=ws)
+        torch.cuda.synchronize()
+        v = sv.debug_views(ws, dims)
+        res.append((out, n, v["logits"].clone(), v["row_max"].clone(), v["row_sumexp"].clone(),
+                    v["status"].clone()))
+        del ws
+    for k, (a, b) in enumerate(zip(*res)):
+        assert torch.equal(a, b), f"{KEYS[k]} differs between the layouts"
+    if static:
+        out, n = sv.verify_static(hidden, Wt, draft, q, u)
+        torch.cuda.synchronize()
+        assert torch.equal(out, res[0][0]) and torch.equal(n, res[0][1])
+    del W, Wt, q
+
+
+@pytest.mark.parametrize("B,gamma,d,V,seed", [
+    (1, 4, 1536, 262144, 31),       # R = 5, the one-sequence head shape
+    (8, 4, 1536, 262144, 32),       # R = 40
+    (16, 4, 4096, 128256, 33),      # R = 80
+    (64, 4, 4096, 128256, 34),      # R = 320
+    (256, 4, 4096, 128256, 35),     # R = 1280
+])
+def test_tiled_w_full_shapes(B, gamma, d, V, seed):
+    dev = _dev()
+    _say(f"tiled vs row-major at full shape B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    _full_shape_pair(B, gamma, d, V, seed, dev, static=B * (gamma + 1) <= 40)
+
+
+def test_tiled_w_past_4gib():
+    """262000 x 8200 bf16: both the row-major W (4.297 GB) and its tiled copy
+    (16375 x 257 tiles, 4.309 GB) are past 2^32 bytes, so the many-row GEMM
+    takes 64-bit pointer copies in both layouts; ragged last k step."""
+    import draft_token_verification_02_amd as sv
+    dev = _dev()
+    B, gamma, d, V, seed = 16, 4, 8200, 262000, 36
+    assert sv.tiled_w_bytes(V, d) >= 1 << 32 and V * d * 2 >= 1 << 32
+    _say(f"tiled past 4 GiB B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    _full_shape_pair(B, gamma, d, V, seed, dev)
