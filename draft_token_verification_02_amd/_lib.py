@@ -20,7 +20,7 @@ SV_DEV_BAD_DRAFT, SV_DEV_FALLBACK, SV_DEV_NONFINITE, SV_DEV_BAD_QID = 1, 2, 4, 8
 SV_LMHEAD_LOGITS, SV_LMHEAD_ARGMAX = 1, 2
 SV_W_ROWS, SV_W_TILED = 0, 1
 ABI_VERSION = 5
-STATIC_SCRATCH_BYTES = 48 << 20
+STATIC_SCRATCH_BYTES = 49 << 20
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_workspace_bytes", "spec_verify", "sv_lmhead",
            "sv_accept_and_draw", "spec_verify_greedy", "sv_accept_greedy", "sv_debug_views",
            "spec_verify_sparse_q", "sv_accept_and_draw_sparse_q", "sv_sparse_head_workspace_bytes",

@@ -10,7 +10,7 @@
 
 namespace sv {
 int lmhead_grid(int V);
-hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, bool w_tiled, int R,
+hipError_t launch_lmhead_tiled(const uint16_t* htile, const uint16_t* W, bool w_tiled, int R,
                                int d, int V, float* logits, float* part_max, float* part_sum,
                                int32_t* part_arg, int NPs, int32_t* counters, int n_counters,
                                hipStream_t stream);
@@ -18,7 +18,7 @@ hipError_t launch_lmhead(const uint16_t* hidden, const uint16_t* W, bool w_tiled
                          int V, float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                          int NPs, int grid, int32_t* counters, int n_counters, hipStream_t stream);
 size_t tiled_w_bytes(int V, int d);
-hipError_t launch_tile_w(const uint16_t* W, int V, int d, uint16_t* Wt, hipStream_t stream);
+hipError_t launch_tile_rows(const uint16_t* W, int V, int d, uint16_t* Wt, hipStream_t stream);
 hipError_t launch_greedy(const float* part_max, const int32_t* part_arg, int NP, int NPs, int B,
                          int gamma, int V, const int32_t* draft, int32_t* out_tokens,
                          int32_t* n_accepted, int32_t* target_tokens, int32_t* status,
@@ -83,16 +83,22 @@ sv_status stage1(const uint16_t* hidden, const uint16_t* W, sv_dims dims, void* 
     int32_t* part_arg = with_argmax ? at<int32_t>(ws, L.part_arg) : nullptr;
     const bool w_tiled = dims.w_layout == SV_W_TILED;
     hipError_t e;
-    if (sv::lmhead_use_tiled(L.R, dims.V))
-        e = sv::launch_lmhead_tiled(hidden, W, w_tiled, L.R, dims.d, dims.V, logits,
+    if (sv::lmhead_use_tiled(L.R, dims.V)) {
+        // the many-row GEMM reads the hidden rows tiled as well: a copy in
+        // the workspace, made here (R d bf16 read and written once)
+        uint16_t* htile = at<uint16_t>(ws, L.htile);
+        e = sv::launch_tile_rows(hidden, L.R, dims.d, htile, s);
+        if (e == hipSuccess)
+            e = sv::launch_lmhead_tiled(htile, W, w_tiled, L.R, dims.d, dims.V, logits,
                                     at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
                                     part_arg, L.NPs,
                                     at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
-    else
+    } else {
         e = sv::launch_lmhead(hidden, W, w_tiled, L.R, dims.d, dims.V, logits,
                               at<float>(ws, L.part_max), at<float>(ws, L.part_sum),
                               part_arg, L.NPs, sv::lmhead_grid(dims.V),
                               at<int32_t>(ws, L.counters), dims.B * sv::kCounterStride, s);
+    }
     return e == hipSuccess ? SV_OK : SV_ERR_DEVICE;
 }
 
@@ -277,7 +283,7 @@ sv_status sv_tile_w(const uint16_t* W, int32_t V, int32_t d, uint16_t* W_tiled, 
     if (!W || !W_tiled) return SV_ERR_NULL;
     if (!aligned(W, 16) || !aligned(W_tiled, 16)) return SV_ERR_ALIGN;
     if (tiled_bytes < sv::tiled_w_bytes(V, d)) return SV_ERR_WORKSPACE;
-    return sv::launch_tile_w(W, V, d, W_tiled, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+    return sv::launch_tile_rows(W, V, d, W_tiled, static_cast<hipStream_t>(hip_stream)) == hipSuccess
                ? SV_OK
                : SV_ERR_DEVICE;
 }

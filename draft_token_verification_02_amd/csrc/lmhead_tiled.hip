@@ -176,12 +176,13 @@ __device__ __forceinline__ void read_frags_asm(u32x4 (&fa)[8], u32x4 (&fb)[FR], 
 
 // Two waves per SIMD (one workgroup per CU) with the four-stage ring; four
 // (two workgroups per CU: <= 128 registers) with the three-stage one.
-// WT: W in 1 KB tiles of 16 vocab rows x 32 hidden columns (tile (i, t) at
-// element (i * nk + t) * 512), so each 16-row slice of a stage is one
-// contiguous 1 KB of memory; otherwise [V][d] row-major.
+// htile: the R hidden rows in 1 KB tiles of 16 rows x 32 columns (tile
+// (i, t) at element (i * nk + t) * 512, zero past R and d), so each 16-row
+// slice of a stage is one contiguous 1 KB of memory.  W the same with WT,
+// otherwise [V][d] row-major.
 template <int FR, int S, bool ARG, bool BUF, bool WT>
 __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ? 4 : 2))) void lmhead_big_kernel(
-    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, int R, int d, int V,
+    const uint16_t* __restrict__ htile, const uint16_t* __restrict__ W, int R, int d, int V,
     int nvb, int nrb, float* __restrict__ logits, float* __restrict__ part_max,
     float* __restrict__ part_sum, int32_t* __restrict__ part_arg, int NPs,
     int32_t* __restrict__ counters, int n_counters) {
@@ -221,13 +222,13 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     // This wave's copies: instruction j = wave + m * NW of the stage covers
     // chunks 64 j .. 64 j + 63, lane i chunk 64 j + i: row c / 4, slot c % 4,
     // holding k-chunk g = slot ^ ((row >> 1) & 3) of that row.  Rows past V
-    // (or R) copy the last valid row; their results are never stored.  With
-    // WT one W instruction reads one whole 1 KB tile.  When
+    // (or R) copy the last valid row; their results are never stored.  One
+    // instruction on a tiled operand reads one whole 1 KB tile.  When
     // NI is not a multiple of NW a wave's last j may pass NI: it repeats its
     // previous copy (same bytes to the same place), so every wave issues NIW
     // copies per step and the vmcnt accounting is the same on every wave.
     //
-    // BUF (both matrices under 4 GiB): each copy is a buffer load with the
+    // BUF (both operands under 4 GiB): each copy is a buffer load with the
     // lane's byte offset from the matrix start fixed for the whole walk and
     // the step's k in the resource base, so a copy costs scalar work, one
     // M0 write and the load itself -- no per-lane address arithmetic, which
@@ -242,56 +243,55 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     // row = 16 j + lane / 4 with 16 j a multiple of 8, so (row >> 1) & 3 = (lane >> 3) & 3
     const int goff = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
     const int nk = (d + kBigK - 1) / kBigK;
-    // Element offset of k step 0 of vocab row v.
-    auto w_row = [&](int v) -> size_t {
-        return WT ? (size_t)(v >> 4) * nk * 512 + (v & 15) * kBigK : (size_t)v * d;
-    };
+    // Element offset of k step 0 of row v of a tiled operand, and of W.
+    auto tile_row = [&](int v) -> size_t { return (size_t)(v >> 4) * nk * 512 + (v & 15) * kBigK; };
+    auto w_row = [&](int v) -> size_t { return WT ? tile_row(v) : (size_t)v * d; };
 #pragma unroll
     for (int m = 0; m < NIW; ++m) {
         const int j = wave + m * NW < NI ? wave + m * NW : wave + (m - 1) * NW;
         const int row = j * 16 + (lane >> 2);
-        const size_t elem = (row < TV ? w_row(min(v0 + row, V - 1)) : (size_t)min(r0 + row - TV, R - 1) * d) + goff;
+        const size_t elem = (row < TV ? w_row(min(v0 + row, V - 1)) : tile_row(min(r0 + row - TV, R - 1))) + goff;
         from_w[m] = j < TV / 16;                 // the same for every lane of the instruction
         if constexpr (BUF) voff[m] = (uint32_t)(elem * 2);
-        else src[m] = (row < TV ? W : hidden) + elem;
+        else src[m] = (row < TV ? W : htile) + elem;
         dst[m] = j * 1024;
     }
 
     const bool ragged = d % kBigK != 0;       // the last step has chunks past the end of a row
     auto stage = [&](int s) -> char* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
     // Copies of step t (t >= nk: a repeat of the last step, into a stage no
-    // step reads again, so that every step issues the same copies).  A chunk
-    // past the end of a row copies the row's first chunk instead; the
-    // fragment lanes holding it are zeroed after the read.
-    // With BUF the chunks past the end of a row read the next row's first
-    // bytes instead (or zeros past the matrix): the same fragment lanes are
-    // zeroed all the same.  With WT a W chunk past d reads the tile's zeros.
-    auto copy_k = [&](int t) {
-        t = t < nk ? t : nk - 1;
-        const int k0 = t * kBigK;
+    // step reads again, so that every step issues the same copies), as
+    // element offsets from each copy's step-0 address.  A tiled operand
+    // moves one 1 KB tile per step, and its chunks past d read the tiles'
+    // zeros.  In row-major W a chunk past the end of a row copies the row's
+    // first chunk instead (pointer copies) or reads the next row's first
+    // bytes (buffer copies; zeros past the matrix); the fragment lanes
+    // holding it are zeroed after the read.
+    auto tile_step = [&](int t) { return (t < nk ? t : nk - 1) * kBigK * 16; };
+    auto w_step = [&](int t) {
+        if (WT) return tile_step(t);
+        const int k0 = (t < nk ? t : nk - 1) * kBigK;
         return (BUF || !ragged || k0 + goff < d) ? k0 : -goff;
     };
-    // Elements from a W copy's step-0 address to step t's: k0 row-major,
-    // 16 k0 (one 1 KB tile per step) tiled.
-    auto w_step = [&](int t, int kk) { return WT ? (t < nk ? t : nk - 1) * kBigK * 16 : kk; };
-    // A buffer copy reads from the matrix at the step's k (base) up to the
-    // matrix's end (range): both uniform, so they live in scalar registers.
-    const uint32_t w_bytes = BUF ? (uint32_t)(WT ? (size_t)(V + 15) / 16 * nk * 1024 : (size_t)V * d * 2) : 0u;
-    const uint32_t h_bytes = BUF ? (uint32_t)((size_t)R * d * 2) : 0u;
-    auto copy_one = [&](int m, int kk, int kw, char* st) {
+    // A buffer copy reads from the operand at the step's offset (base) up
+    // to the operand's end (range): both uniform, so they live in scalar
+    // registers.
+    const uint32_t w_bytes = BUF ? (uint32_t)(WT ? tiled_bytes(V, d) : (size_t)V * d * 2) : 0u;
+    const uint32_t h_bytes = BUF ? (uint32_t)tiled_bytes(R, d) : 0u;
+    auto copy_one = [&](int m, int kh, int kw, char* st) {
         auto* l = (__attribute__((address_space(3))) void*)(st + dst[m]);
         if constexpr (BUF) {
-            const uint32_t kb = (uint32_t)(from_w[m] ? kw : kk) * 2u;
-            buffer_copy_lds(from_w[m] ? (const char*)W + kb : (const char*)hidden + kb,
+            const uint32_t kb = (uint32_t)(from_w[m] ? kw : kh) * 2u;
+            buffer_copy_lds(from_w[m] ? (const char*)W + kb : (const char*)htile + kb,
                             (from_w[m] ? w_bytes : h_bytes) - kb, voff[m], l);
         } else {
-            __builtin_amdgcn_global_load_lds((void*)(src[m] + (from_w[m] ? kw : kk)), l, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((void*)(src[m] + (from_w[m] ? kw : kh)), l, 16, 0, 0);
         }
     };
     auto copy = [&](int t, char* st) {
-        const int kk = copy_k(t), kw = w_step(t, kk);
+        const int kh = tile_step(t), kw = w_step(t);
 #pragma unroll
-        for (int m = 0; m < NIW; ++m) copy_one(m, kk, kw, st);
+        for (int m = 0; m < NIW; ++m) copy_one(m, kh, kw, st);
     };
 
     f32x4 acc[FV][FR];
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
     static_assert(NIW <= FV, "one copy per fragment row at most");
     constexpr bool kCopyInRead = S == 4;
     auto mfmas_copy = [&](int t, char* st) {
-        const int kk = copy_k(t), kw = w_step(t, kk);
+        const int kh = tile_step(t), kw = w_step(t);
 #pragma unroll
         for (int a = 0; a < FV; ++a) {
 #pragma unroll
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, fa[a]), __builtin_bit_cast(bf16x8, fb[b]),
                     acc[a][b], 0, 0, 0);
-            if (!kCopyInRead && a < NIW) copy_one(a, kk, kw, st);
+            if (!kCopyInRead && a < NIW) copy_one(a, kh, kw, st);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kBigNT) __attribute__((amdgpu_waves_per_eu(S == 3 ?
 
 
 template <int FR, int S, bool WT>
-hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
+hipError_t launch_big(const uint16_t* htile, const uint16_t* W, int R, int d, int V,
                       float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                       int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
     using C = BigCfg<FR>;
@@ -508,32 +508,31 @@ hipError_t launch_big(const uint16_t* hidden, const uint16_t* W, int R, int d, i
     const int nblocks = nvb * nrb;
     const int grid = (nblocks + kXcds - 1) / kXcds * kXcds;
     // Buffer copies need both matrices' byte sizes to fit the 32-bit range.
-    const size_t nk = (d + kBigK - 1) / kBigK;
-    const size_t w_bytes = WT ? (size_t)(V + 15) / 16 * nk * 1024 : (size_t)V * d * 2;
-    const bool buf = w_bytes < (1ull << 32) && (size_t)R * d * 2 < (1ull << 32);
+    const size_t w_bytes = WT ? tiled_bytes(V, d) : (size_t)V * d * 2;
+    const bool buf = w_bytes < (1ull << 32) && tiled_bytes(R, d) < (1ull << 32);
     const dim3 g(grid), blk(kBigNT);
     if (part_arg && buf)
         lmhead_big_kernel<FR, S, true, true, WT><<<g, blk, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+            htile, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     else if (part_arg)
         lmhead_big_kernel<FR, S, true, false, WT><<<g, blk, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+            htile, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     else if (buf)
         lmhead_big_kernel<FR, S, false, true, WT><<<g, blk, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+            htile, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     else
         lmhead_big_kernel<FR, S, false, false, WT><<<g, blk, 0, stream>>>(
-            hidden, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
+            htile, W, R, d, V, nvb, nrb, logits, part_max, part_sum, part_arg, NPs, counters, n_counters);
     return hipGetLastError();
 }
 
 template <bool WT>
-hipError_t launch_any(const uint16_t* hidden, const uint16_t* W, int R, int d, int V,
+hipError_t launch_any(const uint16_t* htile, const uint16_t* W, int R, int d, int V,
                       float* logits, float* part_max, float* part_sum, int32_t* part_arg,
                       int NPs, int32_t* counters, int n_counters, hipStream_t stream) {
     // 64 < R <= 128: one 128-row block per W tile, two workgroups per CU.
     if (R <= 128)
-        return launch_big<2, 3, WT>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
+        return launch_big<2, 3, WT>(htile, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
                                     counters, n_counters, stream);
     // The row-block height (64 FR rows) that pads R least, ties to the taller
     // block, whose W tile then serves more rows: R = 320 runs one block of
@@ -542,27 +541,28 @@ hipError_t launch_any(const uint16_t* hidden, const uint16_t* W, int R, int d, i
     for (int fr : {4, 3, 2})
         if ((R + 64 * fr - 1) / (64 * fr) * (64 * fr) < (R + 64 * FR - 1) / (64 * FR) * (64 * FR)) FR = fr;
     switch (FR) {
-        case 5: return launch_big<5, 4, WT>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+        case 5: return launch_big<5, 4, WT>(htile, W, R, d, V, logits, part_max, part_sum, part_arg,
                                             NPs, counters, n_counters, stream);
-        case 4: return launch_big<4, 4, WT>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+        case 4: return launch_big<4, 4, WT>(htile, W, R, d, V, logits, part_max, part_sum, part_arg,
                                             NPs, counters, n_counters, stream);
-        case 3: return launch_big<3, 4, WT>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+        case 3: return launch_big<3, 4, WT>(htile, W, R, d, V, logits, part_max, part_sum, part_arg,
                                             NPs, counters, n_counters, stream);
-        default: return launch_big<2, 4, WT>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+        default: return launch_big<2, 4, WT>(htile, W, R, d, V, logits, part_max, part_sum, part_arg,
                                              NPs, counters, n_counters, stream);
     }
 }
 
 }  // namespace
 
-// w_tiled: W is in the 16 x 32 tile layout, else [V][d] row-major.
-hipError_t launch_lmhead_tiled(const uint16_t* hidden, const uint16_t* W, bool w_tiled, int R,
+// htile: the hidden rows in the 16 x 32 tile layout; w_tiled: W in it too,
+// else [V][d] row-major.
+hipError_t launch_lmhead_tiled(const uint16_t* htile, const uint16_t* W, bool w_tiled, int R,
                                int d, int V, float* logits, float* part_max, float* part_sum,
                                int32_t* part_arg, int NPs, int32_t* counters, int n_counters,
                                hipStream_t stream) {
-    return w_tiled ? launch_any<true>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
+    return w_tiled ? launch_any<true>(htile, W, R, d, V, logits, part_max, part_sum, part_arg, NPs,
                                       counters, n_counters, stream)
-                   : launch_any<false>(hidden, W, R, d, V, logits, part_max, part_sum, part_arg,
+                   : launch_any<false>(htile, W, R, d, V, logits, part_max, part_sum, part_arg,
                                        NPs, counters, n_counters, stream);
 }
 

@@ -57,8 +57,14 @@ static inline bool lmhead_use_tiled(int R, int V) {
 struct Layout {
     int R, NPs, NC;
     size_t logits, part_max, part_sum, part_arg, row_max, row_sum, status, counters, csum, psum,
-        cwave, pwave, tstate, total;
+        cwave, pwave, tstate, htile, total;
 };
+
+// Bytes of a [N][d] bf16 matrix in 1 KB tiles of 16 rows x 32 columns (rows
+// and columns padded with zeros to whole tiles).
+__host__ __device__ inline size_t tiled_bytes(int N, int d) {
+    return (size_t)((N + 15) / 16) * (size_t)((d + 31) / 32) * 1024;
+}
 
 // The draw's chunk totals, fp64: per (sequence, chunk) the sums of the draw
 // weights (csum [B][NC]) and of p (psum), and the same per wave of the
@@ -75,7 +81,6 @@ constexpr size_t kTreeStateBytes = 32;   // per-sequence walk state of tree veri
 static inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 static inline Layout make_layout(int B, int gamma, int d, int V) {
-    (void)d;
     Layout L;
     L.R = B * (gamma + 1);
     const int np_tiled = lmhead_tiled_partials(V);
@@ -97,6 +102,8 @@ static inline Layout make_layout(int B, int gamma, int d, int V) {
     L.cwave = off;    off = align_up(off + (size_t)B * L.NC * kDrawWaves * sizeof(double), 256);
     L.pwave = off;    off = align_up(off + (size_t)B * L.NC * kDrawWaves * sizeof(double), 256);
     L.tstate = off;   off = align_up(off + (size_t)B * kTreeStateBytes, 256);
+    // the hidden rows in tiles, for the many-row GEMM (written by stage 1)
+    L.htile = off;    off = align_up(off + (lmhead_use_tiled(L.R, V) ? tiled_bytes(L.R, d) : 0), 256);
     L.total = off;
     return L;
 }

@@ -172,7 +172,7 @@ SV_API sv_status spec_verify(const uint16_t *hidden, const uint16_t *W_lmhead,
  * SV_STATIC_SCRATCH_BYTES on every device it runs on, kept until the process
  * ends.  Other arguments, results and conventions as for spec_verify.
  *   - Returns SV_ERR_WORKSPACE, before anything is enqueued, when
- *     sv_workspace_bytes(dims) exceeds SV_STATIC_SCRATCH_BYTES (48 MiB: up
+ *     sv_workspace_bytes(dims) exceeds SV_STATIC_SCRATCH_BYTES (49 MiB: up
  *     to 45 rows at V = 262144, 95 rows at V = 128256).
  *   - Allocates nothing.  The first call on a device looks the array's
  *     address up on the current device (hipGetSymbolAddress); `hip_stream`
@@ -181,7 +181,7 @@ SV_API sv_status spec_verify(const uint16_t *hidden, const uint16_t *W_lmhead,
  *     call's contents (no clearing is needed: the step resets what it uses).
  *     Calls that can overlap on one device (different streams or host
  *     threads) race on it; the caller must serialise them. */
-#define SV_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+#define SV_STATIC_SCRATCH_BYTES ((size_t)49 << 20)
 SV_API sv_status spec_verify_static(const uint16_t *hidden, const uint16_t *W_lmhead,
                              const int32_t *draft_tokens, const float *q, const float *uniforms,
                              sv_dims dims, int32_t *out_tokens, int32_t *n_accepted,

@@ -60,15 +60,18 @@ def _ws(B, g, d, V):
 def test_workspace_bytes():
     assert _ws(1, 4, 1536, 262144) >= 5 * 262144 * 4
     assert _ws(256, 4, 4096, 128256) >= 1280 * 128256 * 4
-    # grows with R and V; independent of d
+    # grows with R and V; independent of d up to 64 rows, beyond which it
+    # also holds the hidden rows in tiles (16-row, 32-column, zero-padded)
     assert _ws(2, 4, 64, 1000) > _ws(1, 4, 64, 1000)
-    assert _ws(1, 4, 64, 2000) > _ws(1, 4, 64, 1000)
+    assert _ws(1, 4, 64, 1000) > _ws(1, 4, 64, 1000 - 256)
     assert _ws(1, 4, 64, 1000) == _ws(1, 4, 4096, 1000)
-    assert _ws(1, 4, 64, 1000) % 256 == 0
+    assert _ws(12, 4, 40, 1000) == _ws(12, 4, 4096, 1000)               # 60 rows
+    assert _ws(13, 4, 4096, 1000) - _ws(13, 4, 40, 1000) == 80 * 4096 * 2 - 80 * 64 * 2
+    assert _ws(1, 4, 64, 1000) % 256 == 0 and _ws(13, 4, 40, 1000) % 256 == 0
 
 
 def test_static_workspace_limits_as_documented():
-    """The header's figures for the static workspace (48 MiB): gamma = 4 steps
+    """The header's figures for the static workspace (49 MiB): gamma = 4 steps
     of up to 45 rows at V = 262144 and 95 rows at V = 128256 fit, the next
     batch size does not."""
     lim = _lib.STATIC_SCRATCH_BYTES
@@ -353,7 +356,7 @@ def test_static_entry_point_errors_return_before_any_device_call():
         args = [p] * 7
         args[i] = None
         assert lib.spec_verify_static(*args[:5], ok, *args[5:], None) == _lib.SV_ERR_NULL
-    # the largest row counts the 48 MiB array holds at the two head shapes
+    # the largest row counts the 49 MiB array holds at the two head shapes
     assert _lib.workspace_bytes(_lib.Dims(9, 4, 1536, 262144)) <= _lib.STATIC_SCRATCH_BYTES
     assert _lib.workspace_bytes(_lib.Dims(19, 4, 4096, 128256)) <= _lib.STATIC_SCRATCH_BYTES
 
