@@ -215,6 +215,59 @@ def test_lmhead_w_near_4gib(d):
     del W, q, ws
 
 
+def test_lmhead_hidden_rows_past_4gib():
+    """Many rows at the largest hidden size: 32770 rows x 65536 bf16 (4.29 GB),
+    whose tiled copy in the workspace (2049 x 2048 tiles, 4.297 GB) is past
+    2^32 bytes, so the many-row GEMM copies the hidden rows through 64-bit
+    pointers (192-row blocks; a ragged last row tile).  Sampled logits --
+    first, last and ragged-tile rows -- against the oracle's exact dot
+    products to the stated fp32 summation bound, each sampled row's
+    normaliser against the GPU's own logits, and the outputs valid."""
+    import torch
+    import draft_token_verification_02_amd as sv
+    from draft_token_verification_02_amd import _lib
+    dev = _dev()
+    B, gamma, d, V, seed = 6554, 4, 65536, 256, 92
+    R_ = B * (gamma + 1)
+    assert R_ * d * 2 >= 1 << 32 and -(-R_ // 16) * d * 2 * 16 >= 1 << 32
+    _say(f"hidden rows past 4 GiB B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    g = torch.Generator(device=dev).manual_seed(seed)
+    W = torch.randn((V, d), generator=g, device=dev, dtype=torch.bfloat16).mul_(0.004)
+    hidden = torch.randn((B, gamma + 1, d), generator=g, device=dev, dtype=torch.bfloat16)
+    draft = torch.randint(0, V, (B, gamma), generator=g, device=dev, dtype=torch.int32)
+    q = torch.rand((B, gamma, V), generator=g, device=dev) + 0.5
+    q /= q.sum(dim=-1, keepdim=True)
+    u = torch.rand((B, gamma + 1), generator=g, device=dev).clamp_(min=1e-6)
+    dims = sv.dims_of(hidden, W)
+    ws = sv.new_workspace(dims, dev)
+    out, n = sv.verify(hidden, W, draft, q, u, workspace=ws)
+    torch.cuda.synchronize()
+    views = sv.debug_views(ws, dims)
+    rows = [0, 1, 17, 16383, 32767, 32768, R_ - 1]
+    h_bits = hidden.reshape(R_, d)[rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    w_bits = W.view(torch.int16).cpu().numpy().view(np.uint16)
+    exact = R.lmhead_logits(h_bits, w_bits)
+    absdot = R.bf16_to_f64(h_bits).__abs__() @ R.bf16_to_f64(w_bits).__abs__().T
+    L = views["logits"][rows].double().cpu().numpy()
+    nu = (d - 1) * 2.0 ** -24
+    bound = nu / (1 - nu) * absdot
+    err = np.abs(L - exact)
+    _say(f"max |dlogit| {err.max():.3e}, largest allowed {bound.max():.3e}")
+    assert np.all(err <= bound), f"logit error {err.max()} beyond its bound"
+    for i, r in enumerate(rows):
+        m = L[i].max()
+        assert float(views["row_max"][r]) == m
+        s_ref = np.exp(L[i] - m).sum()
+        assert abs(float(views["row_sumexp"][r]) - s_ref) <= 2e-5 * s_ref
+    n_h = n.cpu().numpy()
+    o_h = out.cpu().numpy()
+    assert np.all((n_h >= 0) & (n_h <= gamma))
+    ok = np.take_along_axis(o_h, n_h[:, None].astype(np.int64), axis=1)[:, 0]
+    assert np.all((ok >= 0) & (ok < V))
+    assert np.all(views["status"].cpu().numpy() == 0)
+    del hidden, q, ws
+
+
 def test_large_logits_stated_bound():
     """Logits near 90 (W std 0.5, d = 1536), where fp32 accumulation alone moves
     p by more than 1e-5: the error chain the library documents, checked link by
