@@ -148,7 +148,9 @@ SV_API sv_status sv_tile_w(const uint16_t *W, int32_t V, int32_t d, uint16_t *W_
 
 /* Bytes of device workspace one call needs for `dims`; 0 if dims are invalid.
  * The workspace holds the fp32 logits [R][V], the per-row softmax
- * normalisers and argmax candidates, and the draw's partial sums.  Its contents need no
+ * normalisers and argmax candidates, the draw's partial sums and, for
+ * R > 64 rows, the hidden rows copied into the tiled layout of SV_W_TILED
+ * (the many-row LM-head GEMM reads them so).  Its contents need no
  * initialisation and are overwritten by every call. */
 SV_API size_t sv_workspace_bytes(sv_dims dims);
 
