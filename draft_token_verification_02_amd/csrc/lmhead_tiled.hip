@@ -16,10 +16,16 @@
 // A workgroup of eight waves computes 256 vocab entries x TR = 64 FR rows;
 // both operands go from memory straight into LDS through a ring of k steps,
 // and the waves take turns between MFMAs and fragment reads (ping-pong).
+// The hidden rows arrive in 1 KB tiles of 16 rows x 32 columns (the caller
+// tiles them into the workspace first), W in the same tiles or [V][d]
+// row-major: a tiled operand's 16-row slice of a k step is one contiguous
+// 1 KB, where a row-major one takes half of a 128-byte line from each of
+// 16 rows and the next k step the other half.
 //
 //   R <= 128: FR = 2 with a three-stage ring -- 74 KB of LDS (76 KB with
-//     argmax partials) and <= 128 registers, so two workgroups share a CU and one's loads, epilogue and
-//     stores overlap the other's MFMAs.  HBM-bound: W is streamed once.
+//     argmax partials) and <= 128 registers, so two workgroups share a CU
+//     and one's loads, epilogue and stores overlap the other's MFMAs.
+//     HBM-bound: W is streamed once.
 //   R > 128: FR in {5, 4, 3, 2}, whichever pads R least (ties to the taller
 //     block), with a four-stage ring, one workgroup per CU.  At R = 1280 the
 //     GEMM is MFMA-bound and four 320-row blocks share each W tile.
