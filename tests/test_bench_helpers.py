@@ -71,3 +71,25 @@ def test_comment_edits_keep_summaries_current(tmp_path, monkeypatch):
     assert bench.traffic_from_counters("w1") is None
     # comment markers inside string literals are code
     assert bench.code_text('s = "a // b"; // c') == 's = "a // b";'
+
+
+def test_committed_summaries_match_the_kernel_sources():
+    """Every counter summary under profiles/ was taken on the kernels as they
+    are: its recorded hash matches the current sources, so bench.py reports
+    its figures.  (A change to a kernel's code without new counter runs
+    fails here.)"""
+    import glob
+    files = sorted(glob.glob(os.path.join(bench.PROFILES, "*_counters.json")) +
+                   glob.glob(os.path.join(bench.PROFILES, "*_mfma_util.json")))
+    assert files, "no committed counter summaries"
+    stale = []
+    for path in files:
+        with open(path) as f:
+            c = json.load(f)
+        if c["kernel_hash"] != bench.source_hash(c["kernel_sources"]):
+            stale.append(os.path.basename(path))
+    assert not stale, f"summaries older than their kernels: {stale}"
+    workloads = {json.load(open(p))["workload"] for p in files}
+    for w in ("sweep_b256_s0.5", "sweep_b256_s0.5+tiled_w", "gemma_e2b"):
+        assert w in workloads
+        assert bench.traffic_from_counters(w) is not None
