@@ -195,3 +195,35 @@ def test_tiled_w_past_4gib():
     assert sv.tiled_w_bytes(V, d) >= 1 << 32 and V * d * 2 >= 1 << 32
     _say(f"tiled past 4 GiB B={B} gamma={gamma} d={d} V={V} seed={seed}")
     _full_shape_pair(B, gamma, d, V, seed, dev)
+
+
+@pytest.mark.parametrize("B,gamma,d,V,C,M,k,seed", [
+    (3, 4, 128, 4096, 128, 32, 8, 1),
+    (8, 4, 1536, 262144, 2048, 128, 32, 0),
+])
+def test_tiled_w_in_the_drafter_chain(B, gamma, d, V, C, M, k, seed):
+    """The sparse head reads W row-major; the verification after it may take
+    the tiled copy (a deployment keeps both): the chain's outputs must be
+    bitwise those of the all-row-major chain."""
+    import torch
+    import draft_token_verification_02_amd as sv
+    dev = _dev()
+    _say(f"tiled chain B={B} gamma={gamma} d={d} V={V} C={C} M={M} k={k} seed={seed}")
+    x = I.drafter_chain(B, gamma, d, V, C, M, k, seed=seed)
+    t = parity.to_device(x, dev)
+    ids, vals, _ = sv.sparse_head(t["h_draft_bits"], t["W_bits"], t["centroid_bits"],
+                                  t["members"], k)
+    K = k * M
+    res = []
+    for w in (t["W_bits"], sv.tile_w(t["W_bits"])):
+        dims = sv.dims_of(t["hidden_bits"], w)
+        ws = sv.new_workspace(dims, dev)
+        out, n = sv.verify_sparse_q(t["hidden_bits"], w, t["draft"], ids.view(B, gamma, K),
+                                    vals.view(B, gamma, K), t["uniforms"], workspace=ws)
+        torch.cuda.synchronize()
+        v = sv.debug_views(ws, dims)
+        res.append([out.cpu().numpy(), n.cpu().numpy(), v["logits"].cpu().numpy(),
+                    v["status"].cpu().numpy()])
+        del ws
+    for k_, (a, b) in enumerate(zip(*res)):
+        np.testing.assert_array_equal(b, a, err_msg=("out", "n", "logits", "status")[k_])

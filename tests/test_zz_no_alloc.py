@@ -75,17 +75,19 @@ def test_static_workspace_rejects_dims_beyond_its_size():
     assert _lib.workspace_bytes(_lib.Dims(B, gamma, d, V)) > _lib.STATIC_SCRATCH_BYTES
 
 
-@pytest.mark.parametrize("B, gamma, d, V, seed", [(4, 4, 256, 30000, 51), (16, 4, 512, 20000, 52)])
-def test_static_workspace_replays_in_a_graph(B, gamma, d, V, seed):
+@pytest.mark.parametrize("B, gamma, d, V, seed, tiled", [(4, 4, 256, 30000, 51, False),
+                                                         (16, 4, 512, 20000, 52, False),
+                                                         (16, 4, 512, 20000, 53, True)])
+def test_static_workspace_replays_in_a_graph(B, gamma, d, V, seed, tiled):
     import torch
     import draft_token_verification_02_amd as sv
     assert torch.cuda.is_available(), "no ROCm device"
     sv.library()
     dev = torch.device("cuda:0")
-    _say(f"static workspace in a graph B={B} gamma={gamma} d={d} V={V} seed={seed}")
+    _say(f"static workspace in a graph B={B} gamma={gamma} d={d} V={V} seed={seed} tiled W={tiled}")
     x = I.custom(B, gamma, d, V, seed=seed, sigma=0.8, w_std=parity.small_w_std(d))
     t = parity.to_device(x, dev)
-    args = (t["hidden_bits"], t["W_bits"], t["draft"], t["q"], t["uniforms"])
+    args = (t["hidden_bits"], parity.gpu_w(t, tiled), t["draft"], t["q"], t["uniforms"])
     ref_out, ref_n = sv.verify_static(*args)          # eager; also resolves the array's address
     torch.cuda.synchronize()
     ref_out, ref_n = ref_out.cpu().numpy(), ref_n.cpu().numpy()
