@@ -104,8 +104,8 @@ typedef struct {
  *               of 16 rows 2d bytes apart.  Results are bitwise identical to
  *               SV_W_ROWS (same products, same summation order); only the
  *               speed differs: measured at d = 1536 and 4096, the LM head
- *               runs 4-8% faster tiled at 26 to 416 rows, the same at 1280,
- *               and from 4% slower to 2% faster below 26 rows.
+ *               runs 4-12% faster tiled from 26 to 1280 rows, and from 4%
+ *               slower to 2% faster below 26 rows.
  * The entry points that take sv_dims accept either; sv_sparse_head reads
  * W_lmhead as SV_W_ROWS only. */
 #define SV_W_ROWS 0
